@@ -1,0 +1,184 @@
+"""ctypes wrapper of the float64 CPU oracle (``oracle/tt_oracle.c``).
+
+Test infrastructure only: the test suite, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg are its only users. It shares no code with the
+HIP library and never calls it.
+
+Each function follows the Nemotron-TwoTower paper (arXiv 2606.26493):
+``block_attn`` is Eq. (1) of section 2.1, ``lse_merge`` is the split of
+Eq. (1)'s concatenated key set into disjoint parts, ``conf_unmask`` is the
+ConfidenceSample step of Algorithm 2 (section 2.2, "Sampling").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libtt_oracle.so")
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+
+
+def load(path: Optional[str] = None):
+    """Load (building first if absent) the oracle library; a path selects another build."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _b
+            _b.build()
+        _lib = _bind(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+def _bind(lib):
+    lib.oracle_block_attn.restype = _I
+    lib.oracle_block_attn.argtypes = [_I, _I, _I, _I, _I, _I, ctypes.c_double, _P, _P, _P, _I, _P, _I,
+                                      _P, _P, _P, _I, _P, _P, _P]
+    lib.oracle_lse_merge.restype = _I
+    lib.oracle_lse_merge.argtypes = [_I, _I, _I, _P, _P, _P, _P]
+    lib.oracle_conf_unmask.restype = _I
+    lib.oracle_conf_unmask.argtypes = [_I, _I, _I, _I, ctypes.c_longlong, _P, _P, _P, ctypes.c_double,
+                                       ctypes.c_double, _I, _P, _P, _P, _P, _P]
+    lib.oracle_num_threads.restype = _I
+    return lib
+
+
+class use_library:
+    """Context manager: route the wrappers to another build of the oracle
+    (the mutation tests load deliberately broken copies this way)."""
+
+    def __init__(self, path: str):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        self._saved = _lib
+        _lib = _bind(ctypes.CDLL(self.path))
+        return _lib
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self._saved
+        return False
+
+
+def num_threads() -> int:
+    return int(load().oracle_num_threads())
+
+
+def _raw(t: Optional[torch.Tensor]):
+    """(numpy array kept alive, pointer, dtype code) of a CPU tensor, widened as-is."""
+    if t is None:
+        return None, None, None
+    t = t.detach().to("cpu").contiguous()
+    if t.dtype == torch.bfloat16:
+        a = t.view(torch.int16).numpy().view(np.uint16)
+        code = 1
+    elif t.dtype == torch.float32:
+        a = t.numpy()
+        code = 0
+    else:
+        raise TypeError(f"oracle inputs are float32 or bfloat16, got {t.dtype}")
+    return a, a.ctypes.data, code
+
+
+def _i32(t) -> np.ndarray:
+    if isinstance(t, torch.Tensor):
+        t = t.detach().to("cpu")
+        return np.ascontiguousarray(t.numpy().astype(np.int32))
+    return np.ascontiguousarray(np.asarray(t, dtype=np.int32))
+
+
+def all_rows(B: int, Hq: int, S: int) -> np.ndarray:
+    """Every (b, h, s) triple, in [B][Hq][S] order."""
+    b, h, s = np.meshgrid(np.arange(B), np.arange(Hq), np.arange(S), indexing="ij")
+    return np.stack([b.ravel(), h.ravel(), s.ravel()], axis=1).astype(np.int32)
+
+
+def block_attn(Q, Kc, Vc, page_table, ctx_len, Kd=None, Vd=None, *, page_size: int,
+               scale: float, rows=None):
+    """Eq. (1) for the selected (b, h, s) rows (all rows when ``rows`` is None).
+
+    Returns (O, LSE) as float64 numpy arrays: with ``rows=None`` they have the
+    shapes [B][S][Hq][D] and [B][Hq][S]; otherwise [n][D] and [n].
+    """
+    B, S, Hq, D = Q.shape
+    Hkv = Kc.shape[1]
+    if Kc.shape[2] != page_size:
+        raise ValueError("Kc's third dimension must be page_size")
+    qa, qp, dt = _raw(Q)
+    ka, kp, dk = _raw(Kc)
+    va, vp, _ = _raw(Vc)
+    kda, kdp, _ = _raw(Kd)
+    vda, vdp, _ = _raw(Vd)
+    if dk != dt:
+        raise TypeError("Q and the cache must share a dtype")
+    pt = _i32(page_table).reshape(B, -1)
+    cl = _i32(ctx_len)
+    full = rows is None
+    r = all_rows(B, Hq, S) if full else _i32(rows).reshape(-1, 3)
+    n = r.shape[0]
+    O = np.zeros((n, D), np.float64)
+    L = np.zeros((n,), np.float64)
+    rc = load().oracle_block_attn(dt, B, S, Hq, Hkv, D, float(scale), qp, kp, vp, int(page_size),
+                                  pt.ctypes.data, pt.shape[1], cl.ctypes.data, kdp, vdp, n,
+                                  r.ctypes.data, O.ctypes.data, L.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_block_attn rejected its arguments")
+    del qa, ka, va, kda, vda
+    if full:
+        O = O.reshape(B, Hq, S, D).transpose(0, 2, 1, 3).copy()
+        L = L.reshape(B, Hq, S)
+    return O, L
+
+
+def lse_merge(O_parts, lse_parts):
+    """O_parts [P][n][D], lse_parts [P][n] (float64) -> (O [n][D], lse [n])."""
+    Op = np.ascontiguousarray(np.asarray(O_parts, dtype=np.float64))
+    lp = np.ascontiguousarray(np.asarray(lse_parts, dtype=np.float64))
+    P, n, D = Op.shape
+    O = np.zeros((n, D), np.float64)
+    L = np.zeros((n,), np.float64)
+    rc = load().oracle_lse_merge(P, n, D, Op.ctypes.data, lp.ctypes.data, O.ctypes.data, L.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_lse_merge rejected its arguments")
+    return O, L
+
+
+def conf_unmask(logits, mask, tokens, *, gamma: float, temperature: float, steps_left: int):
+    """One ConfidenceSample step. ``gamma`` and ``temperature`` are used as given
+    (pass float32-rounded values to mirror a float32 caller).
+
+    Returns dict(tokens, mask, conf, argmax, num_masked) as numpy arrays.
+    """
+    B, S, V = logits.shape
+    la, lp, dt = _raw(logits)
+    mk = np.ascontiguousarray(np.asarray(mask.cpu() if isinstance(mask, torch.Tensor) else mask,
+                                         dtype=np.uint8))
+    tk = _i32(tokens)
+    tok_out = np.zeros((B, S), np.int32)
+    mask_out = np.zeros((B, S), np.uint8)
+    conf = np.zeros((B, S), np.float64)
+    am = np.zeros((B, S), np.int32)
+    nm = np.zeros((B,), np.int32)
+    rc = load().oracle_conf_unmask(dt, B, S, V, V, lp, mk.ctypes.data, tk.ctypes.data, float(gamma),
+                                   float(temperature), int(steps_left), tok_out.ctypes.data,
+                                   mask_out.ctypes.data, conf.ctypes.data, am.ctypes.data, nm.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_conf_unmask rejected its arguments")
+    del la
+    return dict(tokens=tok_out, mask=mask_out, conf=conf, argmax=am, num_masked=nm)
+
+
+def f32(x: float) -> float:
+    """x rounded to float32, as a float32 caller hands it to the library."""
+    return float(np.float32(x))
