@@ -1,0 +1,265 @@
+// ConfidenceSample (Nemotron-TwoTower, arXiv 2606.26493, section 2.2
+// "Sampling", Algorithm 2): one step of confidence unmasking.
+//
+// Kernel 1 (vocab_reduce): one pass over the logits of every MASKED row
+// (unmasked rows are never read), gridded over rows x vocabulary splits. Each
+// thread streams 16-byte chunks and keeps (max, first index of the max,
+// sum of exp2((x - max) * log2(e)/temperature)); triples merge exactly across
+// threads and splits, ties at the max going to the lower index.
+// Kernel 2 (unmask_select): one wavefront per sequence, one lane per block
+// position: confidence = 1/sum, then the commit rule -- every position above
+// gamma if there are at least ceil(M/steps_left) of them, else the
+// ceil(M/steps_left) most confident (ties to the lower position).
+#include <limits.h>
+
+#include "tt_internal.h"
+
+namespace tt {
+namespace {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+struct Triple {
+    float m;
+    int a;
+    float z;
+    float pad;
+};
+
+struct UArgs {
+    const void* logits;
+    long long stride;
+    const uint8_t* mask_in;
+    uint8_t* mask_out;
+    int* tokens;
+    float* conf;
+    int* num_masked;
+    Triple* part;  // [n_vsplit][B*S]
+    int B, S, V, n_vsplit, steps_left;
+    float gamma, c;  // c = log2(e) / temperature
+};
+
+__device__ __forceinline__ void combine(float& m, int& a, float& z, float m2, int a2, float z2, float c) {
+    const float M = fmaxf(m, m2);
+    float zz = 0.f;
+    if (M != -INFINITY) {
+        if (m != -INFINITY) zz += z * __builtin_amdgcn_exp2f((m - M) * c);
+        if (m2 != -INFINITY) zz += z2 * __builtin_amdgcn_exp2f((m2 - M) * c);
+    }
+    a = m > m2 ? a : (m2 > m ? a2 : min(a, a2));
+    m = M;
+    z = zz;
+}
+
+// fold 8 consecutive logits starting at index v into (m, a, z)
+__device__ __forceinline__ void fold8(const float (&x)[8], int v, float& m, int& a, float& z, float c) {
+    float cm = x[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) cm = fmaxf(cm, x[k]);
+    if (cm > m) {
+        if (m != -INFINITY) z *= __builtin_amdgcn_exp2f((m - cm) * c);
+        int k = 7;
+#pragma unroll
+        for (int kk = 7; kk >= 0; --kk) if (x[kk] == cm) k = kk;
+        a = v + k;
+        m = cm;
+    }
+    if (m != -INFINITY) {
+        const float mc = m * c;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) z += __builtin_amdgcn_exp2f(__builtin_fmaf(x[k], c, -mc));
+    }
+}
+
+__device__ __forceinline__ void unpack(const u32x4& r, float (&x)[8]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        x[2 * k] = __uint_as_float(r[k] << 16);
+        x[2 * k + 1] = __uint_as_float(r[k] & 0xffff0000u);
+    }
+}
+
+// Element k of a row, widened to float.
+template <bool BF16>
+__device__ __forceinline__ float elem(const void* row, int k) {
+    if (BF16) return __uint_as_float((unsigned)static_cast<const uint16_t*>(row)[k] << 16);
+    return static_cast<const float*>(row)[k];
+}
+
+// Fold elements [lo, hi) (hi - lo <= 8) of a row as one padded chunk.
+template <bool BF16>
+__device__ __forceinline__ void fold_scalar(const void* row, int lo, int hi, float& m, int& a, float& z, float c) {
+    float f[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) f[k] = lo + k < hi ? elem<BF16>(row, lo + k) : -INFINITY;
+    fold8(f, lo, m, a, z, c);
+}
+
+// A row is cut as: a head of a0 < 8 elements up to the first 16-byte boundary,
+// nfull aligned chunks of 8 elements, and a tail of fewer than 8. Split k of the
+// grid takes an equal share of the chunks; split 0 also takes the head and the
+// last split the tail. Each thread visits its elements in increasing index
+// order, so the strict max update keeps the lowest index among its ties.
+template <bool BF16>
+__global__ __launch_bounds__(256) void vocab_reduce(UArgs a) {
+    const int row = blockIdx.x;
+    const int split = blockIdx.y;
+    if (!a.mask_in[row]) return;
+    constexpr int ES = BF16 ? 2 : 4;
+    const char* rp = static_cast<const char*>(a.logits) + (long long)row * a.stride * ES;
+    int a0 = (int)(((16u - (unsigned)(reinterpret_cast<uintptr_t>(rp) & 15u)) & 15u) / ES);
+    if (a0 > a.V) a0 = a.V;
+    const int nfull = (a.V - a0) / 8;
+    const int per = (nfull + a.n_vsplit - 1) / a.n_vsplit;
+    const int c0 = min(nfull, split * per), c1 = min(nfull, c0 + per);
+    float m = -INFINITY, z = 0.f;
+    int am = INT_MAX;
+    const float c = a.c;
+    if (split == 0 && threadIdx.x == 0 && a0 > 0) fold_scalar<BF16>(rp, 0, a0, m, am, z, c);
+    const char* body = rp + a0 * ES;  // 16-byte aligned
+    int ch = c0 + threadIdx.x;
+    if (BF16) {
+        for (; ch + 3 * 256 < c1; ch += 4 * 256) {
+            u32x4 r[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) r[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(body + (ch + k * 256) * 16));
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                float f[8];
+                unpack(r[k], f);
+                fold8(f, a0 + (ch + k * 256) * 8, m, am, z, c);
+            }
+        }
+        for (; ch < c1; ch += 256) {
+            const u32x4 r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(body + ch * 16));
+            float f[8];
+            unpack(r, f);
+            fold8(f, a0 + ch * 8, m, am, z, c);
+        }
+    } else {
+        for (; ch + 256 < c1; ch += 2 * 256) {
+            u32x4 r[4];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                r[2 * k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(body + (ch + k * 256) * 32));
+                r[2 * k + 1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(body + (ch + k * 256) * 32 + 16));
+            }
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                float f[8];
+                for (int e = 0; e < 4; ++e) { f[e] = __uint_as_float(r[2 * k][e]); f[4 + e] = __uint_as_float(r[2 * k + 1][e]); }
+                fold8(f, a0 + (ch + k * 256) * 8, m, am, z, c);
+            }
+        }
+        for (; ch < c1; ch += 256) {
+            const u32x4 r0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(body + ch * 32));
+            const u32x4 r1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(body + ch * 32 + 16));
+            float f[8];
+            for (int e = 0; e < 4; ++e) { f[e] = __uint_as_float(r0[e]); f[4 + e] = __uint_as_float(r1[e]); }
+            fold8(f, a0 + ch * 8, m, am, z, c);
+        }
+    }
+    const int t0 = a0 + nfull * 8;
+    if (split == a.n_vsplit - 1 && threadIdx.x == 0 && t0 < a.V) fold_scalar<BF16>(rp, t0, a.V, m, am, z, c);
+    // block reduction: wavefront shuffles, then across the 4 wavefronts
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const float m2 = __shfl_xor(m, off);
+        const int a2 = __shfl_xor(am, off);
+        const float z2 = __shfl_xor(z, off);
+        combine(m, am, z, m2, a2, z2, c);
+    }
+    __shared__ Triple sh[4];
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) sh[w] = Triple{m, am, z, 0.f};
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int k = 1; k < 4; ++k) combine(m, am, z, sh[k].m, sh[k].a, sh[k].z, c);
+        a.part[(long long)split * a.B * a.S + row] = Triple{m, am, z, 0.f};
+    }
+}
+
+__global__ __launch_bounds__(64) void unmask_select(UArgs a) {
+    const int b = blockIdx.x;
+    const int l = threadIdx.x;
+    const bool inb = l < a.S;
+    const long long row = (long long)b * a.S + l;
+    const bool masked = inb && a.mask_in[row] != 0;
+    float m = -INFINITY, z = 0.f;
+    int am = INT_MAX;
+    if (masked) {
+        for (int k = 0; k < a.n_vsplit; ++k) {
+            const Triple t = a.part[(long long)k * a.B * a.S + row];
+            combine(m, am, z, t.m, t.a, t.z, a.c);
+        }
+    }
+    const float conf = masked ? 1.f / z : -INFINITY;
+    const unsigned long long mmask = __ballot(masked);
+    const int M = __popcll(mmask);
+    const int kmin = (M + a.steps_left - 1) / a.steps_left;
+    const bool pass = masked && conf > a.gamma;
+    const int npass = __popcll(__ballot(pass));
+    bool commit;
+    if (npass >= kmin) {
+        commit = pass;
+    } else {
+        int rank = 0;
+        for (int j = 0; j < 64; ++j) {
+            const float cj = __shfl(conf, j);
+            const bool mj = (mmask >> j) & 1ull;
+            if (mj && (cj > conf || (cj == conf && j < l))) ++rank;
+        }
+        commit = masked && rank < kmin;
+    }
+    const int ncommit = __popcll(__ballot(commit));
+    if (inb) {
+        const uint8_t old = a.mask_in[row];
+        if (commit) a.tokens[row] = am;
+        a.mask_out[row] = commit ? 0 : old;
+        if (masked && a.conf) a.conf[row] = conf;
+    }
+    if (l == 0 && a.num_masked) a.num_masked[b] = M - ncommit;
+}
+
+}  // namespace
+
+UnmaskPlan plan_unmask(const tt_conf_unmask_params& p, int n_cu) {
+    UnmaskPlan pl{};
+    const long long rows = (long long)p.B * p.S;
+    const int cu = n_cu > 0 ? n_cu : 256;
+    // enough workgroups to cover the chip about 8 times, at least 2048 logits each
+    long long want = rows > 0 ? (8LL * cu + rows - 1) / rows : 1;
+    long long cap = (p.V + 2047) / 2048;
+    if (want > cap) want = cap;
+    if (want < 1) want = 1;
+    if (want > 64) want = 64;
+    pl.n_vsplit = (int)want;
+    pl.ws_total = (size_t)pl.n_vsplit * (size_t)rows * sizeof(Triple);
+    return pl;
+}
+
+tt_status launch_unmask(const tt_conf_unmask_params& p, const UnmaskPlan& pl, void* ws, hipStream_t s) {
+    UArgs a{};
+    a.logits = p.logits;
+    a.stride = p.logits_stride_row;
+    a.mask_in = p.mask_in;
+    a.mask_out = p.mask_out;
+    a.tokens = p.tokens;
+    a.conf = p.conf;
+    a.num_masked = p.num_masked;
+    a.part = static_cast<Triple*>(ws);
+    a.B = p.B; a.S = p.S; a.V = p.V;
+    a.n_vsplit = pl.n_vsplit;
+    a.steps_left = p.steps_left;
+    a.gamma = p.gamma;
+    a.c = 1.44269504088896340736f / p.temperature;
+    const dim3 grid(p.B * p.S, pl.n_vsplit);
+    if (p.dtype == TT_BF16)
+        hipLaunchKernelGGL(vocab_reduce<true>, grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(vocab_reduce<false>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(unmask_select, dim3(p.B), dim3(64), 0, s, a);
+    return hipGetLastError() == hipSuccess ? TT_OK : TT_ERR_HIP;
+}
+
+}  // namespace tt

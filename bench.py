@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of the TwoTower block-diffusion hot path on one MI355X.
+
+One step = one whole block of Algorithm 2 (Nemotron-TwoTower, arXiv 2606.26493,
+section 2.2) over a batch: the block starts fully masked; each denoising step
+r = 1..T runs the Eq. (1) block attention of all six attention layers (each
+against its own layer-aligned context cache) and then one ConfidenceSample
+(threshold gamma, steps left T-r+1); the loop stops once every position is
+committed. The denoiser layers between attention and the logits need trained
+weights and are not part of this path: each step's logits are synthetic
+(N(0,1) plus a spike of height 0.5*t at a fixed target), drawn in advance and
+resident in HBM, as are the six caches.
+
+Default workload ("loop"): batch 32, block S=16, T=16, prefix 8192 tokens,
+32 query / 2 KV heads, head_dim 128, bf16, vocabulary 131072, gamma 0.8,
+temperature 0.1. The JSON line reports noisy-block tokens per second per
+attention layer (B*S*layers*steps / time), the attention call's roofline, and
+the CPU oracle on a bounded sample as a baseline.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload loop|single|ragged|long]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from attention_eq_block_amd import api, synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "noisy-block tokens/s per attn layer (S=16); achieved HBM TB/s vs peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Layer:
+    """One attention layer's inputs on the GPU plus its prepared call."""
+
+    def __init__(self, case, layer, workspace=None):
+        inp = synth.make_attn_inputs(case, seed=0, layer=layer, device="cuda")
+        self.inp = inp
+        self.case = case
+        self.p = api.attn_params(inp["Q"], inp["Kc"], inp["Vc"], inp["page_table"], inp["ctx_len"], inp["Kd"],
+                                 inp["Vd"], page_size=inp["page_size"], max_ctx_len=case.max_ctx_len,
+                                 scale=inp["scale"])
+        self.out, self.lse = self.p._keep
+        nb = api.block_attn_workspace_bytes(self.p)
+        self.ws = workspace if workspace is not None else torch.empty(nb, dtype=torch.uint8, device="cuda")
+        self.nb = nb
+
+    def __call__(self, stream):
+        rc = api.lib().tt_block_attn(self.p, self.ws.data_ptr(), self.nb, stream)
+        if rc:
+            raise RuntimeError(f"tt_block_attn failed: {api.status_string(rc)}")
+
+
+def cpu_baseline_loop(layers, logits, case, ucase, budget_s=12.0):
+    """The float64 oracle on whole sequences of the same workload (one layer's attention
+    per sequence plus one unmask step), scaled to tokens/s per attention layer."""
+    import oracle
+
+    S = case.S
+    L0 = layers[0].inp
+    per = case.pages_of(case.ctx_lens[0])
+
+    def sub(b0, b1):
+        pages = L0["page_table"][b0:b1].cpu()
+        lo = int(pages.min())
+        hi = int(pages.max()) + 1
+        return dict(Q=L0["Q"][b0:b1].cpu(), Kc=L0["Kc"][lo:hi].cpu(), Vc=L0["Vc"][lo:hi].cpu(),
+                    page_table=(pages - lo).to(torch.int32), ctx_len=L0["ctx_len"][b0:b1].cpu(),
+                    Kd=L0["Kd"][b0:b1].cpu(), Vd=L0["Vd"][b0:b1].cpu())
+
+    def run(n):
+        d = sub(0, n)
+        t0 = time.perf_counter()
+        oracle.block_attn(d["Q"], d["Kc"], d["Vc"], d["page_table"], d["ctx_len"], d["Kd"], d["Vd"],
+                          page_size=case.page_size, scale=1.0 / math.sqrt(case.D))
+        t1 = time.perf_counter()
+        x = logits[0][:n].cpu()
+        tok, mk = synth.make_mask_state(n, S)
+        oracle.conf_unmask(x, mk, tok, gamma=oracle.f32(ucase.gamma), temperature=oracle.f32(ucase.temperature),
+                           steps_left=synth.LOOP_STEPS)
+        t2 = time.perf_counter()
+        return t1 - t0, t2 - t1
+
+    ta, tu = run(1)
+    n = max(1, min(case.B, int(budget_s / max(1e-3, synth.LOOP_LAYERS * ta + tu))))
+    if n > 1:
+        ta, tu = run(n)
+    per_seq_step = synth.LOOP_LAYERS * ta + tu  # one denoising step of n sequences (6 layers + unmask)
+    value = n * S * synth.LOOP_LAYERS / per_seq_step
+    del per
+    return dict(value=value, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"{n} of {case.B} sequences: one layer's Eq. (1) attention (prefix {case.ctx_lens[0]}, "
+                       f"S={S}, 32/2 heads, d={case.D}) timed {ta:.2f} s and one unmask step timed {tu:.2f} s; "
+                       f"a denoising step counted as 6 attention layers plus one unmask")
+
+
+def run_loop(args):
+    case = synth.attn_case("loop")
+    ucase = synth.unmask_case("loop", temperature=args.temperature, gamma=args.gamma)
+    B, S, T, NL = case.B, case.S, synth.LOOP_STEPS, synth.LOOP_LAYERS
+    log(f"[bench] building {NL} layer caches of {case.kv_bytes() / 1e6:.0f} MB and {T} logit steps on the GPU")
+    layers = []
+    for i in range(NL):
+        layers.append(Layer(case, i, workspace=layers[0].ws if layers else None))
+    targets = synth.spike_targets(B, S, ucase.V, seed=0, device="cuda")
+    logits = [synth.make_logits(ucase, seed=0, step=r, spike=0.5 * r, targets=targets, device="cuda")
+              for r in range(1, T + 1)]
+    tokens = torch.empty((B, S), dtype=torch.int32, device="cuda")
+    mask = torch.empty((B, S), dtype=torch.uint8, device="cuda")
+    nmask = torch.empty((B,), dtype=torch.int32, device="cuda")
+    nm_host = torch.empty((B,), dtype=torch.int32, pin_memory=True)
+    up = api.unmask_params(logits[0], mask, tokens, gamma=ucase.gamma, temperature=ucase.temperature,
+                           steps_left=T, num_masked=nmask)
+    uws = torch.empty(max(16, api.conf_unmask_workspace_bytes(up)), dtype=torch.uint8, device="cuda")
+    lib = api.lib()
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(T)]
+
+    def block(timing=False):
+        tokens.fill_(synth.MASK_TOKEN_ID)
+        mask.fill_(1)
+        steps = 0
+        for r in range(1, T + 1):
+            if timing:
+                ev[r - 1][0].record(stream)
+            for L in layers:
+                L(sh)
+            if timing:
+                ev[r - 1][1].record(stream)
+            up.logits = logits[r - 1].data_ptr()
+            up.steps_left = T - r + 1
+            rc = lib.tt_conf_unmask(up, uws.data_ptr(), uws.numel(), sh)
+            if rc:
+                raise RuntimeError(f"tt_conf_unmask failed: {api.status_string(rc)}")
+            steps = r
+            nm_host.copy_(nmask, non_blocking=True)
+            stream.synchronize()
+            if int(nm_host.sum()) == 0:
+                break
+        return steps
+
+    log("[bench] warmup")
+    for _ in range(args.warmup):
+        block()
+    torch.cuda.synchronize()
+    log("[bench] timed")
+    attn_ms, n_attn_steps, total_steps = 0.0, 0, 0
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        n = block(timing=True)
+        total_steps += n
+        torch.cuda.synchronize()
+        for r in range(n):
+            attn_ms += ev[r][0].elapsed_time(ev[r][1])
+        n_attn_steps += n
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_block = wall * 1e3 / args.steps
+    steps_per_block = total_steps / args.steps
+    value = B * S * NL * total_steps / wall
+    call_ms = attn_ms / (n_attn_steps * NL)
+    algo = case.algorithmic_bytes()
+    achieved = algo / (call_ms * 1e-3) / 1e9
+    assert torch.isfinite(layers[0].out.float()).all()
+    log(f"[bench] {steps_per_block:.2f} steps/block, {ms_per_block:.3f} ms/block, attention call {call_ms * 1e3:.1f} us")
+    res = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_block, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "full-block denoise loop (Algorithm 2): batch 32, S=16, T=16, 6 attention layers, "
+                               "prefix 8192, 32 q / 2 kv heads, head_dim 128, V=131072, gamma 0.8, temperature 0.1",
+                   "global_batch": B, "seq_len": case.ctx_lens[0] + S, "parallelism": "none",
+                   "denoise_steps_per_block": steps_per_block, "blocks_per_s": B * args.steps / wall,
+                   "attn_call_us": call_ms * 1e3, "attn_call_tokens_per_s": B * S / (call_ms * 1e-3)},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "tt_block_attn (attn_bf16_kernel + attn_bf16_finalize), one layer",
+                     "algorithmic_bytes": algo},
+    }
+    if not args.no_cpu:
+        log("[bench] cpu baseline (oracle)")
+        res["cpu_baseline"] = cpu_baseline_loop(layers, logits, case, ucase)
+    return res
+
+
+def run_single(args, name):
+    """Diagnostic: one attention layer of another workload (plus its unmask for 'ragged')."""
+    case = synth.attn_case(name)
+    L = Layer(case, 0)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    for _ in range(args.warmup):
+        L(sh)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        L(sh)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    call_ms = e0.elapsed_time(e1) / args.steps
+    algo = case.algorithmic_bytes()
+    achieved = algo / (call_ms * 1e-3) / 1e9
+    flops = case.flops()
+    res = {"metric": METRIC, "value": case.B * case.S / (call_ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": call_ms, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": f"single attention layer, {name}: B={case.B}, S={case.S}, "
+                                  f"{case.Hq}/{case.Hkv} heads, d={case.D}, max prefix {case.max_ctx_len}",
+                      "global_batch": case.B, "seq_len": case.max_ctx_len + case.S, "parallelism": "none",
+                      "tflops": flops / (call_ms * 1e-3) / 1e12},
+           "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": achieved / HBM_PEAK_GBS, "traffic": None}}
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="loop", choices=["loop", "single", "ragged", "long"])
+    ap.add_argument("--gamma", type=float, default=0.8)
+    ap.add_argument("--temperature", type=float, default=0.1)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (the data-parallel "
+              "sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    res = run_loop(args) if args.workload == "loop" else run_single(args, args.workload)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

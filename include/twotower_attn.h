@@ -1,0 +1,218 @@
+/*
+ * libtwotower_attn -- the TwoTower denoiser's block-attention step and its
+ * confidence-unmask SampleStep, for AMD Instinct MI355X (gfx950).
+ *
+ * Method: "Nemotron-TwoTower: Diffusion Language Modeling with Pretrained
+ * Autoregressive Context" (arXiv 2606.26493).
+ *   - tt_block_attn: section 2.1 ("Bidirectional attention"), Eq. (1). The S
+ *     queries of the noisy block b at denoiser layer i attend to the
+ *     concatenation of the context tower's layer-i KV cache for the clean
+ *     prefix (blocks before b) and the denoiser's own layer-i KV for block b.
+ *   - tt_lse_merge: the concatenation in Eq. (1) split into disjoint key
+ *     sets; partial attentions over the parts combine exactly through their
+ *     log-sum-exp values.
+ *   - tt_conf_unmask: section 2.2 ("Sampling"), Algorithm 2, the
+ *     ConfidenceSample step: commit the masked predictions whose confidence
+ *     exceeds gamma, so that the block still completes within the steps left.
+ *
+ * Conventions shared by every call:
+ *   - Pointers named as tensors are DEVICE pointers owned by the caller. The
+ *     library allocates no device memory; scratch comes from a caller-owned
+ *     workspace of at least tt_*_workspace_bytes(...) bytes.
+ *   - Calls are asynchronous on the caller's stream and never synchronise the
+ *     host. A returned TT_OK means the work was enqueued.
+ *   - Arguments are validated on the host before anything is launched; a
+ *     non-TT_OK status means nothing was enqueued (except TT_ERR_HIP, which
+ *     reports a failed launch).
+ *   - Element strides count elements, not bytes; the innermost dimension
+ *     (head_dim or vocabulary) is always contiguous. For tt_block_attn and
+ *     tt_lse_merge, tensor base pointers must be 16-byte aligned and strides
+ *     multiples of 16 bytes; tt_conf_unmask takes any element-aligned rows.
+ *   - Calls that share a workspace must not overlap in time (same stream or
+ *     ordered streams). Calls with distinct workspaces are independent; the
+ *     library keeps no state besides a per-device cache of the CU count.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef TWOTOWER_ATTN_H
+#define TWOTOWER_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TT_ABI_VERSION 1
+
+typedef enum tt_status {
+    TT_OK = 0,
+    TT_ERR_NULL = 1,        /* a required pointer is NULL */
+    TT_ERR_SHAPE = 2,       /* inconsistent or out-of-range sizes or strides */
+    TT_ERR_DTYPE = 3,       /* unsupported element type combination */
+    TT_ERR_UNSUPPORTED = 4, /* valid but not implemented (head_dim, alignment) */
+    TT_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
+    TT_ERR_ARG = 6,         /* bad scalar argument (NaN gamma, temperature <= 0, ...) */
+    TT_ERR_HIP = 7          /* the HIP runtime reported an error */
+} tt_status;
+
+typedef enum tt_dtype {
+    TT_F32 = 0,  /* IEEE binary32 */
+    TT_BF16 = 1  /* bfloat16 (upper half of binary32); outputs are rounded to nearest even */
+} tt_dtype;
+
+/* ABI version of the loaded library (TT_ABI_VERSION at build time). */
+int tt_abi_version(void);
+
+/* Static description of a status code; never NULL. */
+const char* tt_status_string(tt_status status);
+
+/* ------------------------------------------------------------------------ *
+ * Eq. (1) block attention for one denoiser attention layer
+ * ------------------------------------------------------------------------ *
+ * For sequence b, query head h (KV head g = h / (Hq/Hkv)) and block position
+ * s, the key set is the concatenation of
+ *   - the prefix: tokens j = 0 .. ctx_len[b]-1 of the context tower's cache
+ *     for this layer (pass the context cache of the same layer index: the
+ *     cross-attention is layer-aligned), and
+ *   - the block: tokens 0 .. S-1 of Kden/Vden (every block query sees every
+ *     block key; there is no mask inside the step).
+ * The call computes scaled-dot-product softmax attention over that set:
+ *   sigma_j = softmax_scale * <Q[b][s][h], K_j>,
+ *   O[b][s][h] = sum_j softmax(sigma)_j V_j,
+ *   LSE[b][h][s] = ln sum_j exp(sigma_j)          (natural log, float32).
+ * An empty key set (ctx_len[b] = 0 and Kden = NULL) yields O = 0, LSE = -inf.
+ * Positional encoding, if any, is applied by the caller beforehand.
+ *
+ * Layouts (elements; the head_dim axis contiguous):
+ *   Q          [B][S][Hq][head_dim] at Q + b*q_stride_b + s*q_stride_s + h*q_stride_h
+ *   Kctx, Vctx paged cache [num_pages][Hkv][page_size][head_dim], dense.
+ *              Prefix token j of sequence b is slot j % page_size of page
+ *              page_table[b*max_pages + j / page_size]. A contiguous cache
+ *              is the identity table (one page of page_size = max_ctx_len
+ *              per sequence, or consecutive 16-token pages).
+ *   page_table [B][max_pages] int32 (device). Entries past the last page a
+ *              sequence uses are never read.
+ *   ctx_len    [B] int32 (device): prefix length per sequence, 0 allowed, any
+ *              value (the last page may be partial). Values are clamped to
+ *              [0, min(max_ctx_len, max_pages*page_size)]; a page id outside
+ *              [0, num_pages) reads as zero keys (no fault, wrong result).
+ *   Kden, Vden [B][S][Hkv][head_dim] at base + b*den_stride_b + s*den_stride_s
+ *              + g*den_stride_h; both NULL for a prefix-only partial.
+ *   O          [B][S][Hq][head_dim] of o_dtype at O + b*o_stride_b + ...
+ *   LSE        [B][Hq][S] float32, dense; may be NULL.
+ * dtype is the type of Q, Kctx, Vctx, Kden, Vden; o_dtype is dtype or TT_F32
+ * (float32 partials for a later tt_lse_merge).
+ *
+ * Supported: dtype TT_BF16 (MFMA path, float32 accumulation) or TT_F32
+ * (float32 path); head_dim 64 or 128; 1 <= S <= 64; Hq % Hkv == 0;
+ * page_size a positive multiple of 16; softmax_scale finite and > 0.
+ */
+typedef struct tt_block_attn_params {
+    int32_t dtype;        /* tt_dtype of Q and K/V */
+    int32_t o_dtype;      /* tt_dtype of O: dtype or TT_F32 */
+    int32_t B, S, Hq, Hkv, head_dim;
+    float softmax_scale;  /* usually 1/sqrt(head_dim) */
+
+    const void* Q;
+    int64_t q_stride_b, q_stride_s, q_stride_h;
+
+    const void* Kctx;
+    const void* Vctx;
+    int32_t page_size;
+    int32_t num_pages;
+    const int32_t* page_table;
+    int32_t max_pages;
+    const int32_t* ctx_len;
+    int32_t max_ctx_len;  /* host-side upper bound of ctx_len[] */
+
+    const void* Kden;
+    const void* Vden;
+    int64_t den_stride_b, den_stride_s, den_stride_h;
+
+    void* O;
+    int64_t o_stride_b, o_stride_s, o_stride_h;
+    float* LSE;
+} tt_block_attn_params;
+
+/* Workspace bytes tt_block_attn needs for these parameters (0 if none). The
+ * size depends on B, S, Hq, Hkv, head_dim, dtype and the number of compute
+ * units of the current device. Returns 0 for NULL. */
+size_t tt_block_attn_workspace_bytes(const tt_block_attn_params* p);
+
+/* Enqueue Eq. (1) on `stream`. workspace: device memory of ws_bytes bytes
+ * (may be NULL when the required size is 0). */
+tt_status tt_block_attn(const tt_block_attn_params* p, void* workspace, size_t ws_bytes,
+                        hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * Log-sum-exp merge of P partial attentions over disjoint key sets
+ * ------------------------------------------------------------------------ *
+ * Per row (b, s, h): M = max_p lse_p, w_p = exp(lse_p - M),
+ *   O = sum_p w_p O_p / sum_p w_p,  lse = M + ln(sum_p w_p).
+ * A part with lse = -inf holds no keys and has weight 0; if every part is
+ * empty the row gets O = 0 and lse = -inf. Merging tt_block_attn over the
+ * prefix only (Kden = NULL, o_dtype TT_F32) with tt_block_attn over the block
+ * only (ctx_len = 0) reproduces tt_block_attn over both.
+ *   O_parts   [P][B][S][Hq][d] float32, dense (device)
+ *   lse_parts [P][B][Hq][S] float32, dense (device)
+ *   O_out     [B][S][Hq][d] of o_dtype (TT_F32 or TT_BF16), dense
+ *   lse_out   [B][Hq][S] float32, dense; may be NULL
+ * Requires P >= 1, B >= 0, S >= 1, Hq >= 1, d >= 4 with d % 4 == 0.
+ */
+tt_status tt_lse_merge(int P, const float* O_parts, const float* lse_parts, int B, int S, int Hq,
+                       int d, void* O_out, tt_dtype o_dtype, float* lse_out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * ConfidenceSample: one step of confidence unmasking (Algorithm 2)
+ * ------------------------------------------------------------------------ *
+ * For each sequence b and each MASKED position l (mask_in[b][l] != 0), over
+ * the V logits x of row (b, l):
+ *   a_l    = the smallest v with x_v = max_u x_u        (greedy prediction)
+ *   conf_l = max_v softmax(x / temperature)_v = 1 / sum_v exp((x_v - max x)/temperature)
+ * Let M be the number of masked positions and k = ceil(M / steps_left)
+ * (steps_left = T - r + 1 at step r of T). If at least k masked positions
+ * have conf_l > gamma (strictly), exactly those are committed; otherwise the
+ * k masked positions with the highest confidence are committed (equal
+ * confidences: the lower position first). A committed position gets
+ * tokens[b][l] = a_l and mask_out[b][l] = 0. Every other position keeps its
+ * token and mask; rows of unmasked positions are not read. At steps_left = 1
+ * every masked position is committed, so T steps always complete the block.
+ *
+ *   logits   [B][S][V] (dtype), row (b,l) at logits + (b*S + l)*logits_stride_row
+ *   mask_in  [B][S] uint8, 1 = masked
+ *   mask_out [B][S] uint8 (may alias mask_in)
+ *   tokens   [B][S] int32, in/out (the caller fills masked positions with its
+ *            mask token id)
+ *   conf     [B][S] float32, optional: written for masked positions only
+ *   num_masked [B] int32, optional: masked positions left after the step
+ * Requires 1 <= S <= 64, V >= 1, logits_stride_row >= V, gamma not NaN,
+ * temperature finite and > 0, steps_left >= 1. Rows must hold at least one
+ * finite logit; -inf logits have probability 0.
+ */
+typedef struct tt_conf_unmask_params {
+    int32_t dtype;  /* tt_dtype of logits */
+    int32_t B, S, V;
+    const void* logits;
+    int64_t logits_stride_row;
+    const uint8_t* mask_in;
+    uint8_t* mask_out;
+    int32_t* tokens;
+    float gamma;
+    float temperature;
+    int32_t steps_left;
+    float* conf;
+    int32_t* num_masked;
+} tt_conf_unmask_params;
+
+size_t tt_conf_unmask_workspace_bytes(const tt_conf_unmask_params* p);
+
+tt_status tt_conf_unmask(const tt_conf_unmask_params* p, void* workspace, size_t ws_bytes,
+                         hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TWOTOWER_ATTN_H */

@@ -1,0 +1,159 @@
+"""The C-ABI library on the CPU: it loads, exports every function the header
+declares, and rejects bad arguments on the host before launching anything.
+
+No test here passes a pointer a kernel could dereference: every call is one
+that validation must refuse, so these tests are safe with or without a GPU.
+"""
+import ctypes
+import math
+import subprocess
+
+import pytest
+
+from attention_eq_block_amd import _lib
+from attention_eq_block_amd._lib import TT_BF16, TT_F32, BlockAttnParams, ConfUnmaskParams
+
+FAKE = 0x1000  # never dereferenced: every call below must fail validation first
+
+
+def test_library_loads_and_reports_version():
+    L = _lib.lib()
+    assert L.tt_abi_version() == 1
+
+
+def test_exports_every_header_function():
+    names = _lib.header_functions()
+    assert set(names) == {"tt_abi_version", "tt_status_string", "tt_block_attn", "tt_block_attn_workspace_bytes",
+                          "tt_lse_merge", "tt_conf_unmask", "tt_conf_unmask_workspace_bytes"}
+    L = _lib.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(names) <= exported
+    assert not [s for s in exported if s.startswith("tt_") and s not in names], "undeclared tt_ export"
+
+
+def test_status_strings():
+    L = _lib.lib()
+    for code, name in _lib.STATUS.items():
+        assert L.tt_status_string(code).decode().startswith(name)
+    assert L.tt_status_string(99) == b"unknown tt_status"
+
+
+def attn_ok(**kw):
+    """A parameter set that passes validation in every field except those overridden."""
+    p = BlockAttnParams()
+    p.dtype, p.o_dtype = TT_BF16, TT_BF16
+    p.B, p.S, p.Hq, p.Hkv, p.head_dim = 2, 16, 32, 2, 128
+    p.softmax_scale = 1 / math.sqrt(128)
+    p.Q = p.O = p.Kctx = p.Vctx = p.page_table = p.ctx_len = p.Kden = p.Vden = FAKE
+    p.q_stride_h, p.q_stride_s, p.q_stride_b = 128, 32 * 128, 16 * 32 * 128
+    p.o_stride_h, p.o_stride_s, p.o_stride_b = 128, 32 * 128, 16 * 32 * 128
+    p.den_stride_h, p.den_stride_s, p.den_stride_b = 128, 2 * 128, 16 * 2 * 128
+    p.page_size, p.num_pages, p.max_pages, p.max_ctx_len = 16, 64, 32, 512
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def call_attn(p, ws=None, nbytes=0):
+    return _lib.lib().tt_block_attn(ctypes.byref(p), ws, nbytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=5), 3), (dict(dtype=TT_F32, o_dtype=TT_BF16), 3),
+    (dict(S=0), 2), (dict(S=65), 2), (dict(Hq=30, Hkv=4), 2), (dict(Hkv=0), 2), (dict(B=-1), 2),
+    (dict(head_dim=96), 4), (dict(head_dim=256), 4),
+    (dict(softmax_scale=0.0), 6), (dict(softmax_scale=float("nan")), 6), (dict(softmax_scale=-1.0), 6),
+    (dict(softmax_scale=float("inf")), 6),
+    (dict(Q=None), 1), (dict(O=None), 1), (dict(Kden=None), 1), (dict(Kctx=None), 1), (dict(page_table=None), 1),
+    (dict(ctx_len=None), 1),
+    (dict(page_size=8), 2), (dict(page_size=24), 2), (dict(max_pages=31), 2), (dict(num_pages=0), 2),
+    (dict(max_ctx_len=-3), 2),
+    (dict(Q=FAKE + 8), 4), (dict(O=FAKE + 2), 4), (dict(Kctx=FAKE + 4), 4), (dict(q_stride_h=100), 4),
+    (dict(den_stride_s=4), 4), (dict(o_stride_b=-8), 4),
+    (dict(B=1 << 22, max_ctx_len=1 << 20, max_pages=1 << 16), 2),
+])
+def test_attn_validation(kw, code):
+    rc = call_attn(attn_ok(**kw))
+    assert rc == code, (kw, _lib.STATUS.get(rc))
+
+
+def test_attn_valid_args_need_workspace():
+    assert call_attn(attn_ok()) == 5
+    nb = _lib.lib().tt_block_attn_workspace_bytes(ctypes.byref(attn_ok()))
+    assert nb > 0
+    assert call_attn(attn_ok(), None, nb) == 5
+
+
+def test_attn_zero_batch_is_a_noop():
+    assert call_attn(attn_ok(B=0, Q=None, O=None)) == 0
+
+
+def test_attn_workspace_bytes_of_invalid_is_zero():
+    assert _lib.lib().tt_block_attn_workspace_bytes(ctypes.byref(attn_ok(S=0))) == 0
+    assert _lib.lib().tt_block_attn_workspace_bytes(None) == 0
+    assert _lib.lib().tt_block_attn(None, None, 0, None) == 1
+
+
+def test_attn_workspace_grows_with_batch():
+    L = _lib.lib()
+    a = L.tt_block_attn_workspace_bytes(ctypes.byref(attn_ok(B=2)))
+    b = L.tt_block_attn_workspace_bytes(ctypes.byref(attn_ok(B=64)))
+    assert b > a > 0
+
+
+def unmask_ok(**kw):
+    p = ConfUnmaskParams()
+    p.dtype, p.B, p.S, p.V = TT_BF16, 4, 16, 131072
+    p.logits = p.mask_in = p.mask_out = p.tokens = FAKE
+    p.logits_stride_row = 131072
+    p.gamma, p.temperature, p.steps_left = 0.8, 0.1, 16
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), 3), (dict(S=0), 2), (dict(S=65), 2), (dict(V=0), 2), (dict(logits_stride_row=100), 2),
+    (dict(B=-2), 2), (dict(gamma=float("nan")), 6), (dict(temperature=0.0), 6), (dict(temperature=-1.0), 6),
+    (dict(temperature=float("inf")), 6), (dict(steps_left=0), 6), (dict(logits=None), 1), (dict(mask_in=None), 1),
+    (dict(mask_out=None), 1), (dict(tokens=None), 1), (dict(logits=FAKE + 1), 4),
+    (dict(dtype=TT_F32, logits=FAKE + 2), 4),
+])
+def test_unmask_validation(kw, code):
+    rc = _lib.lib().tt_conf_unmask(ctypes.byref(unmask_ok(**kw)), None, 0, None)
+    assert rc == code, (kw, _lib.STATUS.get(rc))
+
+
+def test_unmask_needs_workspace_and_zero_batch_noop():
+    L = _lib.lib()
+    nb = L.tt_conf_unmask_workspace_bytes(ctypes.byref(unmask_ok()))
+    assert nb > 0
+    assert L.tt_conf_unmask(ctypes.byref(unmask_ok()), None, nb, None) == 5
+    assert L.tt_conf_unmask(ctypes.byref(unmask_ok(B=0, logits=None)), None, 0, None) == 0
+    assert L.tt_conf_unmask(None, None, 0, None) == 1
+
+
+def test_unmask_gamma_extremes_are_valid_arguments():
+    # any non-NaN gamma is allowed; the call then only lacks a workspace
+    for g in (-1.0, 0.0, 1.0, 2.0, float("inf"), float("-inf")):
+        assert _lib.lib().tt_conf_unmask(ctypes.byref(unmask_ok(gamma=g)), None, 0, None) == 5
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, FAKE, FAKE, 1, 1, 1, 64, FAKE, TT_F32, None), 2),
+    ((2, FAKE, FAKE, 1, 0, 1, 64, FAKE, TT_F32, None), 2),
+    ((2, FAKE, FAKE, 1, 1, 0, 64, FAKE, TT_F32, None), 2),
+    ((2, FAKE, FAKE, 1, 1, 1, 6, FAKE, TT_F32, None), 2),
+    ((2, FAKE, FAKE, 1, 1, 1, 64, FAKE, 7, None), 3),
+    ((2, None, FAKE, 1, 1, 1, 64, FAKE, TT_F32, None), 1),
+    ((2, FAKE, FAKE, 1, 1, 1, 64, None, TT_F32, None), 1),
+    ((2, FAKE + 4, FAKE, 1, 1, 1, 64, FAKE, TT_F32, None), 4),
+    ((2, FAKE, FAKE, 1, 1, 1, 12, FAKE, TT_BF16, None), 4),
+    ((2, None, None, 0, 1, 1, 64, None, TT_F32, None), 0),
+])
+def test_merge_validation(args, code):
+    rc = _lib.lib().tt_lse_merge(*args, None)
+    assert rc == code

@@ -1,0 +1,251 @@
+"""tt_block_attn and tt_lse_merge on the GPU against the float64 oracle.
+
+Eq. (1) of Nemotron-TwoTower (arXiv 2606.26493, section 2.1). Small shapes are
+compared element by element; full-size workloads (in the launch configuration the
+benchmark times) on sampled rows. Tolerances are stated in parity.py.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from attention_eq_block_amd import api, synth
+
+from parity import check_attn, check_attn_rows, gpu_attn, oracle_attn, sample_rows, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def case(B, S, Hq, Hkv, D, ctx, dtype=torch.bfloat16, **kw):
+    return synth.AttnCase(B, S, Hq, Hkv, D, list(ctx), dtype=dtype, **kw)
+
+
+def run_full(c, seed=0, what=""):
+    inp = synth.make_attn_inputs(c, seed=seed)
+    O, L = gpu_attn(inp)
+    Or, Lr = oracle_attn(inp)
+    return check_attn(O, L, Or, Lr, c.dtype, what or str(c))
+
+
+# --------------------------------------------------------------------------- workloads
+
+def test_tiny_fp32():
+    """4 q-heads on 1 kv-head, d=64, prefix 48, S=16, float32 (the tiny workload)."""
+    print(run_full(synth.attn_case("tiny")))
+
+
+@pytest.mark.parametrize("variant", ["", "unscaled"])
+def test_single_bf16(variant):
+    """B=1, 32/2 heads, d=128, prefix 4096, S=16 (identity pages)."""
+    print(run_full(synth.attn_case("single", variant)))
+
+
+def test_ragged_bf16_full_size_sampled():
+    """B=64, prefix 16*U{32..512}, shuffled 16-token pages; sampled rows at full size."""
+    c = synth.attn_case("ragged")
+    inp = synth.make_attn_inputs(c, seed=0)
+    O, L = gpu_attn(inp, max_ctx_len=c.max_ctx_len)
+    rows = sample_rows(c.B, c.Hq, c.S, 1500, seed=1)
+    print(check_attn_rows(O, L, inp, rows, c.dtype, "ragged"))
+
+
+def test_ragged_unscaled_small_full_compare():
+    c = case(8, 16, 32, 2, 128, synth.ragged_ctx_lens(8, 16, 1024, 16, seed=3), shuffle_pages=True)
+    print(run_full(c))
+
+
+def test_long_bf16_full_size_sampled():
+    """B=4, prefix 131072, S=32 (two row blocks per kv head); sampled rows."""
+    c = synth.attn_case("long")
+    inp = synth.make_attn_inputs(c, seed=0)
+    O, L = gpu_attn(inp, max_ctx_len=131072)
+    rows = sample_rows(c.B, c.Hq, c.S, 160, seed=2)
+    print(check_attn_rows(O, L, inp, rows, c.dtype, "long"))
+
+
+def test_loop_layer_full_size_sampled():
+    """B=32, prefix 8192, S=16: one of the six layer caches of the denoise loop."""
+    c = synth.attn_case("loop")
+    inp = synth.make_attn_inputs(c, seed=0, layer=3)
+    O, L = gpu_attn(inp, max_ctx_len=8192)
+    rows = sample_rows(c.B, c.Hq, c.S, 600, seed=3)
+    print(check_attn_rows(O, L, inp, rows, c.dtype, "loop"))
+
+
+# --------------------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("ctx", [(0,), (0, 0, 5), (1,), (15, 17, 63, 64, 65), (129, 0, 200)])
+def test_ragged_edges_with_poisoned_tails(ctx):
+    """Prefix lengths off the tile and page grid; the unused slots of the last page and every
+    unused page hold NaN, which must never reach the output."""
+    c = case(len(ctx), 16, 32, 2, 128, ctx, shuffle_pages=True, spare_pages=3, poison_tail=True)
+    print(run_full(c))
+
+
+def test_empty_key_set():
+    """ctx_len = 0 and no block keys: O = 0, LSE = -inf."""
+    c = case(3, 16, 8, 2, 128, [0, 0, 0], with_den=False)
+    inp = synth.make_attn_inputs(c)
+    O, L = gpu_attn(inp)
+    assert torch.all(O.float() == 0) and torch.all(torch.isneginf(L))
+
+
+def test_prefix_only_and_block_only():
+    c = case(3, 16, 32, 2, 128, [300, 64, 1000], with_den=False, shuffle_pages=True)
+    print(run_full(c, what="prefix only"))
+    c = case(3, 16, 32, 2, 128, [0, 0, 0])
+    print(run_full(c, what="block only (empty context: bidirectional attention over the block)"))
+
+
+@pytest.mark.parametrize("S,Hq,Hkv", [(1, 32, 2), (3, 4, 4), (7, 6, 2), (64, 32, 2), (33, 8, 8), (16, 16, 1)])
+def test_shapes(S, Hq, Hkv):
+    """S from 1 to 64, GQA ratios 1..16, row counts S*G that do not fill a 256-row block
+    and ones that need up to four row blocks."""
+    c = case(2, S, Hq, Hkv, 128, [77, 190], shuffle_pages=True)
+    print(run_full(c))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_head_dim_64(dtype):
+    c = case(3, 16, 8, 2, 64, [100, 33, 512], dtype=dtype, shuffle_pages=True)
+    print(run_full(c))
+
+
+@pytest.mark.parametrize("page_size", [32, 48, 64, 256])
+def test_page_sizes(page_size):
+    c = case(3, 16, 32, 2, 128, [100, 700, 257], page_size=page_size, shuffle_pages=True)
+    print(run_full(c))
+
+
+def test_fp32_shapes():
+    c = case(2, 5, 6, 3, 128, [37, 130], dtype=torch.float32, shuffle_pages=True)
+    print(run_full(c))
+
+
+def test_contiguous_cache_as_one_page_per_sequence():
+    """A dense [B][Hkv][L][d] cache is the paged layout with page_size = L and an identity table."""
+    c = case(2, 16, 32, 2, 128, [1024, 1024], page_size=1024)
+    print(run_full(c))
+
+
+def test_strided_views_and_f32_output():
+    """Q, K_den/V_den and O as strided views of larger buffers; bf16 inputs with a float32 O."""
+    c = case(2, 16, 32, 2, 128, [333, 64], shuffle_pages=True)
+    inp = synth.make_attn_inputs(c, seed=4)
+    d = to_dev(inp)
+    Qbig = torch.zeros(2, 16, 40, 128, dtype=torch.bfloat16, device="cuda")
+    Qbig[:, :, 3:35] = d["Q"]
+    Q = Qbig[:, :, 3:35]
+    KVbig = torch.zeros(2, 16, 6, 128, dtype=torch.bfloat16, device="cuda")
+    KVbig[:, :, 1:3] = d["Kd"]
+    Kd = KVbig[:, :, 1:3]
+    KVbig2 = torch.zeros(2, 16, 6, 128, dtype=torch.bfloat16, device="cuda")
+    KVbig2[:, :, 1:3] = d["Vd"]
+    Vd = KVbig2[:, :, 1:3]
+    Obig = torch.full((2, 16, 36, 128), 5.0, dtype=torch.float32, device="cuda")
+    O = Obig[:, :, 2:34]
+    _, L = api.block_attn(Q, d["Kc"], d["Vc"], d["page_table"], d["ctx_len"], Kd, Vd, page_size=16,
+                          max_ctx_len=333, scale=inp["scale"], out=O)
+    torch.cuda.synchronize()
+    Or, Lr = oracle_attn(inp)
+    check_attn(O, L, Or, Lr, torch.float32 if False else torch.bfloat16, "strided")
+    assert torch.all(Obig[:, :, :2] == 5.0) and torch.all(Obig[:, :, 34:] == 5.0), "wrote outside the view"
+    # float32 output of bf16 inputs is accurate beyond bf16 rounding
+    err = (O.double().cpu().numpy() - Or)
+    assert np.abs(err).max() < 2e-2
+
+
+def test_lse_optional_and_batch_zero():
+    c = case(2, 16, 32, 2, 128, [100, 50])
+    inp = synth.make_attn_inputs(c)
+    d = to_dev(inp)
+    p = api.attn_params(d["Q"], d["Kc"], d["Vc"], d["page_table"], d["ctx_len"], d["Kd"], d["Vd"], page_size=16,
+                        max_ctx_len=100, scale=inp["scale"])
+    p.LSE = None
+    ws = torch.empty(api.block_attn_workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    rc = api.lib().tt_block_attn(p, ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert rc == 0
+    Or, _ = oracle_attn(inp)
+    O = p._keep[0]
+    assert np.abs(O.float().cpu().numpy() - Or).max() < 2e-2
+    # B = 0: nothing to do
+    e = torch.empty(0, 16, 32, 128, dtype=torch.bfloat16, device="cuda")
+    api.block_attn(e, d["Kc"], d["Vc"], d["page_table"][:0], d["ctx_len"][:0], None, None, page_size=16,
+                   max_ctx_len=0)
+
+
+# --------------------------------------------------------------------------- properties on the GPU
+
+def test_merge_of_prefix_and_block_partials():
+    """Eq. (1) over the concatenation = tt_lse_merge(prefix-only partial, block-only partial)."""
+    c = case(4, 16, 32, 2, 128, [1000, 64, 0, 4000], shuffle_pages=True)
+    inp = synth.make_attn_inputs(c, seed=6)
+    d = to_dev(inp)
+    Of, Lf = gpu_attn(inp)
+    O1, L1 = api.block_attn(d["Q"], d["Kc"], d["Vc"], d["page_table"], d["ctx_len"], None, None, page_size=16,
+                            max_ctx_len=4000, scale=inp["scale"], o_dtype=torch.float32)
+    zero = torch.zeros_like(d["ctx_len"])
+    O2, L2 = api.block_attn(d["Q"], d["Kc"], d["Vc"], d["page_table"], zero, d["Kd"], d["Vd"], page_size=16,
+                            max_ctx_len=0, scale=inp["scale"], o_dtype=torch.float32)
+    Om, Lm = api.lse_merge(torch.stack([O1, O2]).contiguous(), torch.stack([L1, L2]).contiguous(),
+                           o_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    Or, Lr = oracle_attn(inp)
+    print(check_attn(Om, Lm, Or, Lr, torch.bfloat16, "merged"))
+    assert (Om.float() - Of.float()).abs().max().item() <= 2 ** -7, "merged vs direct"
+
+
+def test_lse_merge_against_oracle_merge():
+    rng = np.random.default_rng(5)
+    P, B, S, Hq, d = 5, 3, 7, 6, 128
+    O = rng.normal(size=(P, B, S, Hq, d)).astype(np.float32)
+    lse = rng.normal(scale=4.0, size=(P, B, Hq, S)).astype(np.float32)
+    lse[1, 0] = -np.inf        # an empty part
+    lse[:, 2, 3] = -np.inf     # rows with every part empty
+    Og, Lg = api.lse_merge(torch.from_numpy(O).cuda(), torch.from_numpy(lse).cuda())
+    torch.cuda.synchronize()
+    n = B * S * Hq
+    Op = O.transpose(0, 1, 2, 3, 4).reshape(P, n, d).astype(np.float64)
+    lp = lse.transpose(0, 1, 3, 2).reshape(P, n).astype(np.float64)
+    Or, Lr = oracle.lse_merge(Op, lp)
+    assert np.abs(Og.cpu().numpy().reshape(n, d) - Or).max() < 1e-5
+    Lg = Lg.cpu().numpy().transpose(0, 2, 1).reshape(n).astype(np.float64)
+    both = np.isneginf(Lg) & np.isneginf(Lr)
+    assert np.all(np.where(both, 0, np.abs(Lg - Lr)) < 1e-5)
+    # bf16 output
+    Ob, _ = api.lse_merge(torch.from_numpy(O).cuda(), torch.from_numpy(lse).cuda(), o_dtype=torch.bfloat16)
+    assert np.abs(Ob.float().cpu().numpy().reshape(n, d) - Or).max() < 2e-2
+
+
+def test_weights_sum_to_one():
+    """V = 1 everywhere: O is exactly 1 after rounding; V = c: O = c."""
+    c = case(3, 16, 32, 2, 128, [900, 17, 4096], shuffle_pages=True, value_scale=3.0)
+    inp = synth.make_attn_inputs(c, seed=2)
+    for val in (1.0, -2.5):
+        inp2 = dict(inp, Vc=torch.full_like(inp["Vc"], val), Vd=torch.full_like(inp["Vd"], val))
+        O, _ = gpu_attn(inp2)
+        assert torch.all(O.float() == val), f"V={val}: {O.float().unique()[:5]}"
+
+
+def test_block_permutation_equivariance():
+    c = case(2, 16, 32, 2, 128, [500, 77], shuffle_pages=True, value_scale=2.0)
+    inp = synth.make_attn_inputs(c, seed=8)
+    O, L = gpu_attn(inp)
+    pi = torch.randperm(16, generator=torch.Generator().manual_seed(1))
+    inp2 = dict(inp, Q=inp["Q"][:, pi].contiguous(), Kd=inp["Kd"][:, pi].contiguous(), Vd=inp["Vd"][:, pi].contiguous())
+    O2, L2 = gpu_attn(inp2)
+    assert (O2.float() - O[:, pi].float()).abs().max().item() <= 2 ** -7
+    assert (L2 - L[:, :, pi]).abs().max().item() <= 1e-3
+
+
+def test_deterministic():
+    c = synth.attn_case("ragged")
+    c.B = 16
+    c.ctx_lens = c.ctx_lens[:16]
+    inp = synth.make_attn_inputs(c, seed=1)
+    O1, L1 = gpu_attn(inp)
+    O2, L2 = gpu_attn(inp)
+    assert torch.equal(O1, O2) and torch.equal(L1, L2)
