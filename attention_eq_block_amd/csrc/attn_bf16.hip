@@ -8,7 +8,8 @@
 // dense 256-row tile and both products are MFMA contractions
 // (v_mfma_f32_32x32x16_bf16, fp32 accumulation):
 //   S^T[key][row] = K[key][:] . Q[row][:]      (A = K tile from LDS, B = Q in registers)
-//   O^T[d][row]  += V^T[d][key] . P^T[key][row] (A = V^T tile from LDS, B = P in registers)
+//   O^T[d][row]  += V^T[d][key] . P^T[key][row] (A = V tile read transposed from LDS,
+//                                                B = P in registers)
 // Computing the transposed score tile puts each lane's scores of one query
 // row in the register layout the second product takes as its B operand, so P
 // never leaves registers. The softmax is online (running max and sum per
@@ -25,6 +26,8 @@
 // (O normalised, LSE) per segment, merged by a second kernel. Segments are
 // numbered so that consecutive ones run on the same XCD, which keeps a pair's
 // partials in one L2.
+#include <type_traits>
+
 #include "tt_internal.h"
 
 namespace tt {
@@ -37,22 +40,34 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;                 // waves per workgroup (two per SIMD)
+constexpr int kNT = kRows / (32 * kWaves); // 32-row MFMA tiles per wave
+constexpr int kThreads = 64 * kWaves;
+constexpr int kFinThreads = 256;
 constexpr float kTau = 8.0f;  // lazy rescale threshold (log2 units)
 constexpr float kLn2 = 0.693147180559945309f;
 
 template <int D>
 struct Cfg {
-    static constexpr int KSTR = D + 8;        // K row stride in LDS (elements), 16-byte pad
-    static constexpr int VSTR = kTile + 8;    // V^T row stride in LDS (elements)
-    static constexpr int K_ELEMS = kTile * KSTR;
-    static constexpr int V_ELEMS = D * VSTR;
-    static constexpr int BUF = K_ELEMS + V_ELEMS;
-    static constexpr int DS = D / 16;         // k-steps of the score product
-    static constexpr int DT = D / 32;         // d tiles of the output product
-    static constexpr int CHUNKS = D / 8;      // 16-byte chunks per K/V row
-    static constexpr int KPT = kTile * CHUNKS / kThreads;  // keys per thread per tile
+    static constexpr int CPR = D / 8;              // 16-byte chunks per K/V row
+    static constexpr int ROWB = D * 2;             // bytes per row (rows are not padded)
+    static constexpr int TILEB = kTile * ROWB;     // bytes of one K (or V) tile
+    static constexpr int STAGEB = 2 * TILEB;       // K then V
+    static constexpr int LPK = kTile * CPR / kThreads;  // 16-byte K (and V) loads per thread per tile
+    static constexpr int DS = D / 16;              // k-steps of the score product
+    static constexpr int DT = D / 32;              // d tiles of the output product
+    static_assert(LPK >= 1 && LPK <= 2, "one or two chunks of K and of V per thread and tile");
 };
+
+// Rows sit unpadded in LDS; the 16-byte chunk c of row r is stored at chunk
+// position c ^ swz(r). Over any 16 consecutive rows (the rows one 16-lane
+// phase of a K-operand read touches) and over the 4-row x 4-chunk blocks of a
+// transposing V read, the swizzle sends the accessed chunks to distinct banks.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
 
 struct Args {
     const uint16_t* Q;
@@ -75,28 +90,30 @@ struct Args {
     float c_log2;  // softmax_scale * log2(e)
 };
 
-__device__ __forceinline__ int seq_len(const Args& a, int b) {
-    return a.ctx_len ? clamp_len(a.ctx_len[b], a.Lmax) : 0;
+__device__ __forceinline__ int seq_len(const Args& a, const int* __restrict__ ctx_len, int b) {
+    return ctx_len ? clamp_len(ctx_len[b], a.Lmax) : 0;
 }
 __device__ __forceinline__ int units_for(const Args& a, int L) { return (L + kTile - 1) / kTile + a.has_den; }
 
 // Block-wide: total units W and, for unit u (u >= 0), the sequence holding it
 // and the first unit of that sequence. For b_prefix >= 0 instead, also the
-// first unit of sequence b_prefix. `sh` is LDS scratch of 260 ints.
-__device__ void scan_units(const Args& a, int u, int b_prefix, int* sh, int& W, int& b_out, int& c_out) {
+// first unit of sequence b_prefix. `sh` is LDS scratch of NTHR + 4 ints.
+template <int NTHR>
+__device__ void scan_units(const Args& a, const int* __restrict__ ctx_len, int u, int b_prefix, int* sh, int& W,
+                           int& b_out, int& c_out) {
     const int t = threadIdx.x;
     const int mult = a.Hkv * a.n_rb;
-    const int chunk = (a.B + kThreads - 1) / kThreads;
+    const int chunk = (a.B + NTHR - 1) / NTHR;
     const int lo = min(a.B, t * chunk), hi = min(a.B, lo + chunk);
     int sum = 0, before = 0;
     for (int b = lo; b < hi; ++b) {
-        const int n = units_for(a, seq_len(a, b)) * mult;
+        const int n = units_for(a, seq_len(a, ctx_len, b)) * mult;
         sum += n;
         if (b < b_prefix) before += n;
     }
     sh[t] = sum;
     __syncthreads();
-    for (int off = 1; off < kThreads; off <<= 1) {
+    for (int off = 1; off < NTHR; off <<= 1) {
         const int v = t >= off ? sh[t - off] : 0;
         __syncthreads();
         sh[t] += v;
@@ -104,23 +121,23 @@ __device__ void scan_units(const Args& a, int u, int b_prefix, int* sh, int& W, 
     }
     const int incl = sh[t];
     const int excl = incl - sum;
-    W = sh[kThreads - 1];
+    W = sh[NTHR - 1];
     __syncthreads();
-    if (t == 0) { sh[256] = 0; sh[257] = 0; sh[258] = 0; }
+    if (t == 0) { sh[NTHR] = 0; sh[NTHR + 1] = 0; sh[NTHR + 2] = 0; }
     __syncthreads();
     if (u >= 0 && u >= excl && u < incl) {
         int c = excl;
         for (int b = lo; b < hi; ++b) {
-            const int n = units_for(a, seq_len(a, b)) * mult;
-            if (u < c + n) { sh[256] = b; sh[257] = c; break; }
+            const int n = units_for(a, seq_len(a, ctx_len, b)) * mult;
+            if (u < c + n) { sh[NTHR] = b; sh[NTHR + 1] = c; break; }
             c += n;
         }
     }
-    if (b_prefix >= 0 && b_prefix >= lo && b_prefix < hi) sh[258] = excl + before;
-    else if (b_prefix >= 0 && b_prefix == a.B && t == kThreads - 1) sh[258] = incl;
+    if (b_prefix >= 0 && b_prefix >= lo && b_prefix < hi) sh[NTHR + 2] = excl + before;
+    else if (b_prefix >= 0 && b_prefix == a.B && t == NTHR - 1) sh[NTHR + 2] = incl;
     __syncthreads();
-    if (u >= 0) { b_out = sh[256]; c_out = sh[257]; }
-    if (b_prefix >= 0) c_out = sh[258];
+    if (u >= 0) { b_out = sh[NTHR]; c_out = sh[NTHR + 1]; }
+    if (b_prefix >= 0) c_out = sh[NTHR + 2];
     __syncthreads();
 }
 
@@ -129,113 +146,141 @@ struct Cur {
     int L, units;    // prefix length, tiles per pair of sequence b
 };
 
-__device__ __forceinline__ void advance(Cur& c, const Args& a) {
+__device__ __forceinline__ void advance(Cur& c, const Args& a, const int* __restrict__ ctx_len) {
     if (++c.t < c.units) return;
     c.t = 0;
     if (++c.pl < a.Hkv * a.n_rb) return;
     c.pl = 0;
     for (;;) {
         if (++c.b >= a.B) { c.units = 1; return; }
-        c.L = seq_len(a, c.b);
+        c.L = seq_len(a, ctx_len, c.b);
         c.units = units_for(a, c.L);
         if (c.units > 0) return;
     }
 }
 
-template <int D>
-struct Regs {
-    u32x4 k[Cfg<D>::KPT];
-    u32x4 v[Cfg<D>::KPT];
-};
-
 __device__ __forceinline__ u32x4 ldg_nt(const uint16_t* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-// global -> registers: this thread's KPT keys x one 16-byte chunk of the tile at c
+// ---- tile loads: global -> registers -> LDS --------------------------------
+// Thread t moves chunk (t + kThreads*i) of each tile: row r = that / CPR, 16-byte
+// chunk c = that % CPR. The rows a wave touches for one i lie in one 16-aligned
+// group of keys, hence in one page, so the page id is wave-uniform (a scalar
+// load, issued one tile ahead of the loads that use it).
 template <int D>
-__device__ __forceinline__ void load_tile(Regs<D>& r, const Cur& c, const Args& a) {
+struct Regs {
+    u32x4 k[Cfg<D>::LPK];
+    u32x4 v[Cfg<D>::LPK];
+};
+
+struct Pages {
+    int p[2];
+};
+
+template <int D>
+__device__ __forceinline__ Pages tile_pages(const Cur& c, const Args& a, const int* __restrict__ page_table) {
+    using C = Cfg<D>;
+    Pages pg{{0, 0}};
+    const int nct = (c.L + kTile - 1) / kTile;
+    if (c.t >= nct) return pg;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int i = 0; i < C::LPK; ++i) {
+        const int r = (wave * 64 + kThreads * i) / C::CPR;  // first row of this wave's block
+        const int j0 = min(c.t * kTile + r, c.L - 1);
+        pg.p[i] = page_table[(long long)c.b * a.max_pages + j0 / a.page_size];
+    }
+    return pg;
+}
+
+// Issue this thread's loads of the tile at c. Loads are unconditional and their
+// registers are not touched until they are stored to LDS: a key past the end of
+// a partial tile reads the tile's last valid key instead (finite, weight exactly
+// 0); a page id outside [0, num_pages) is clamped, so a corrupt table reads
+// wrong data but never faults.
+template <int D>
+__device__ __forceinline__ void load_tile(Regs<D>& r, const Cur& c, const Pages& pg, const Args& a) {
     using C = Cfg<D>;
     const int tid = threadIdx.x;
-    const int kg = tid / C::CHUNKS, ch = tid % C::CHUNKS;
     const int g = c.pl / a.n_rb;
     const int nct = (c.L + kTile - 1) / kTile;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    if (c.t < nct) {
-        const int j0 = c.t * kTile + kg * C::KPT;  // KPT consecutive keys, all in one page
-        int page = -1;
-        if (j0 < c.L) page = a.page_table[(long long)c.b * a.max_pages + j0 / a.page_size];
-        const bool ok = page >= 0 && page < a.num_pages;
-        const long long base = (((long long)(ok ? page : 0) * a.Hkv + g) * a.page_size + j0 % a.page_size) * D + ch * 8;
 #pragma unroll
-        for (int i = 0; i < C::KPT; ++i) {
-            const bool valid = ok && (j0 + i < c.L);
-            r.k[i] = valid ? ldg_nt(a.Kc + base + (long long)i * D) : z;
-            r.v[i] = valid ? ldg_nt(a.Vc + base + (long long)i * D) : z;
+    for (int i = 0; i < C::LPK; ++i) {
+        const int q = tid + kThreads * i;
+        const int row = q / C::CPR, ch = q % C::CPR;
+        long long off;
+        const uint16_t* kb;
+        const uint16_t* vb;
+        if (c.t < nct) {
+            const int page = min(max(pg.p[i], 0), a.num_pages - 1);
+            const int j = min(c.t * kTile + row, c.L - 1);
+            off = (((long long)page * a.Hkv + g) * a.page_size + j % a.page_size) * D + ch * 8;
+            kb = a.Kc;
+            vb = a.Vc;
+        } else {
+            const int j = min(row, a.S - 1);
+            off = (long long)c.b * a.dsb + (long long)j * a.dss + (long long)g * a.dsh + ch * 8;
+            kb = a.Kd;
+            vb = a.Vd;
         }
-    } else {
-        const long long base = (long long)c.b * a.dsb + (long long)g * a.dsh + ch * 8;
-#pragma unroll
-        for (int i = 0; i < C::KPT; ++i) {
-            const int j = kg * C::KPT + i;
-            const bool valid = j < a.S;
-            r.k[i] = valid ? ldg_nt(a.Kd + base + (long long)j * a.dss) : z;
-            r.v[i] = valid ? ldg_nt(a.Vd + base + (long long)j * a.dss) : z;
-        }
+        r.k[i] = ldg_nt(kb + off);
+        r.v[i] = ldg_nt(vb + off);
     }
 }
 
-// position of key k inside a V^T row: within each 16-key group, bits 2 and 3
-// of the key index are swapped, so the 8 keys one lane feeds to a 16-key
-// MFMA step (keys 4h..4h+3 and 8+4h..8+4h+3, h = lane / 32) sit contiguously.
-__device__ __forceinline__ int vpos(int k) {
-    return (k & ~15) | ((k & 4) << 1) | ((k & 8) >> 1) | (k & 3);
-}
-
+// registers -> LDS stage, chunk c of row r at chunk position c ^ swz(r)
 template <int D>
-__device__ __forceinline__ void store_tile(const Regs<D>& r, uint16_t* buf) {
+__device__ __forceinline__ void store_tile(const Regs<D>& r, uint8_t* stage) {
     using C = Cfg<D>;
     const int tid = threadIdx.x;
-    const int kg = tid / C::CHUNKS, ch = tid % C::CHUNKS;
-    uint16_t* Ks = buf;
-    uint16_t* Vt = buf + C::K_ELEMS;
 #pragma unroll
-    for (int i = 0; i < C::KPT; ++i)
-        *reinterpret_cast<u32x4*>(Ks + (kg * C::KPT + i) * C::KSTR + ch * 8) = r.k[i];
-    const int pos = vpos(kg * C::KPT);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int sh = (e & 1) * 16;
-        unsigned w[C::KPT / 2];
-#pragma unroll
-        for (int i = 0; i < C::KPT / 2; ++i) {
-            const unsigned lo = (r.v[2 * i][e >> 1] >> sh) & 0xffffu;
-            const unsigned hi = (r.v[2 * i + 1][e >> 1] >> sh) & 0xffffu;
-            w[i] = lo | (hi << 16);
-        }
-        uint16_t* dst = Vt + (ch * 8 + e) * C::VSTR + pos;
-        if constexpr (C::KPT == 4) {
-            u32x2 v2 = {w[0], w[1]};
-            *reinterpret_cast<u32x2*>(dst) = v2;
-        } else {
-            *reinterpret_cast<unsigned*>(dst) = w[0];
-        }
+    for (int i = 0; i < C::LPK; ++i) {
+        const int q = tid + kThreads * i;
+        const int row = q / C::CPR, ch = q % C::CPR;
+        const int off = row * C::ROWB + 16 * (ch ^ swz<D>(row));
+        *reinterpret_cast<u32x4*>(stage + off) = r.k[i];
+        *reinterpret_cast<u32x4*>(stage + C::TILEB + off) = r.v[i];
     }
 }
 
-__device__ __forceinline__ bf16x8 lds16(const uint16_t* p) {
+// Workgroup barrier ordering LDS accesses only: waits for this wave's own LDS
+// writes, not for the global loads in flight (a plain __syncthreads() would
+// wait for those too and drain the prefetch).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ bf16x8 lds16(const uint8_t* p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 
-__device__ __forceinline__ float bf16_round(float x) {
-    return (float)(__bf16)x;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes, lane i
+// receives element i%4 of the 8-byte rows read by lanes i/4, i/4+4, i/4+8, i/4+12.
+__device__ __forceinline__ i16x4 lds_tr(const uint8_t* p) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
 }
 
+// Per-wave state carried across tiles.
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a) {
+struct State {
+    bf16x8 qf[kNT][Cfg<D>::DS];
+    f32x16 oacc[Cfg<D>::DT][kNT];
+    float m2[kNT], lsum[kNT];
+    int piece_t0;
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const int* __restrict__ page_table,
+                                                                const int* __restrict__ ctx_len) {
     using C = Cfg<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::BUF];
-    __shared__ int sh[260];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * C::STAGEB];
+    __shared__ int sh[kThreads + 4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -246,89 +291,124 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a) {
     const int seg = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
 
     int W, b0, c0;
-    // first pass: total units (needed for the segment length)
-    scan_units(a, -1, -1, sh, W, b0, c0);
+    scan_units<kThreads>(a, ctx_len, -1, -1, sh, W, b0, c0);  // total units W
+    W = __builtin_amdgcn_readfirstlane(W);                     // uniform: keep the walk in scalar registers
     const int seg_len = (W + a.n_seg - 1) / a.n_seg;
     const int u0 = seg * seg_len;
     const int u1 = min(W, u0 + seg_len);
     if (u0 >= u1) return;
-    scan_units(a, u0, -1, sh, W, b0, c0);
+    scan_units<kThreads>(a, ctx_len, u0, -1, sh, W, b0, c0);
+    b0 = __builtin_amdgcn_readfirstlane(b0);
+    c0 = __builtin_amdgcn_readfirstlane(c0);
 
-    Cur nxt;
-    nxt.b = b0;
-    nxt.L = seq_len(a, b0);
-    nxt.units = units_for(a, nxt.L);
+    Cur cc;  // tile being computed
+    cc.b = b0;
+    cc.L = seq_len(a, ctx_len, b0);
+    cc.units = units_for(a, cc.L);
     {
         const int off = u0 - c0;
-        nxt.pl = off / nxt.units;
-        nxt.t = off % nxt.units;
+        cc.pl = off / cc.units;
+        cc.t = off % cc.units;
     }
     const int mult = a.Hkv * a.n_rb;
 
-    Regs<D> regs;
-    load_tile<D>(regs, nxt, a);
-
-    bf16x8 qf[2][C::DS];
-    f32x16 oacc[C::DT][2];
-    float m2[2], lsum[2];
-    int piece_t0 = 0;
-    int buf = 0;
-
-    for (int u = u0; u < u1; ++u) {
-        uint16_t* B = smem + buf * C::BUF;
-        store_tile<D>(regs, B);
-        __syncthreads();
-        const Cur c = nxt;
-        if (u + 1 < u1) {
-            advance(nxt, a);
-            load_tile<D>(regs, nxt, a);
-        }
-        const int g = c.pl / a.n_rb, rb = c.pl % a.n_rb;
-        if (u == u0 || c.t == 0) {
-            // new piece: query rows of (b, g, rb), fresh softmax state
-            piece_t0 = c.t;
+    // Two register sets carry tiles u+1 and u+2 while tile u is computed: a tile's
+    // loads are issued two iterations before its registers are stored to LDS.
+    Regs<D> R[2];
+    Cur cl = cc;  // next tile to load
+    int ul = u0;
+    Pages pg = tile_pages<D>(cl, a, page_table);
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                const int rr = rb * kRows + wave * 64 + nt * 32 + l32;
+    for (int k = 0; k < 2; ++k) {
+        if (ul < u1) {
+            load_tile<D>(R[k], cl, pg, a);
+            if (++ul < u1) {
+                advance(cl, a, ctx_len);
+                pg = tile_pages<D>(cl, a, page_table);
+            }
+        }
+    }
+
+    State<D> st;
+    st.piece_t0 = 0;
+    // lane-constant parts of the swizzled LDS addresses
+    const int ksw = swz<D>(l32);
+    const int vrow = 4 * hl + ((lane & 15) >> 2);
+    const int vsw0 = swz<D>(vrow), vsw1 = swz<D>(vrow + 8);
+    const int vchunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    const int vbyte = 8 * (lane & 1);
+
+    // one tile; S is the register set / LDS stage of tile u (u - u0 even: 0)
+    auto step = [&](auto S_, int u) __attribute__((always_inline)) {
+        constexpr int S = decltype(S_)::value;
+        uint8_t* stage = smem + S * C::STAGEB;
+        store_tile<D>(R[S], stage);
+        lds_barrier();
+        const Cur c = cc;
+        const int g = c.pl / a.n_rb, rb = c.pl % a.n_rb;
+        const bool new_piece = u == u0 || c.t == 0;
+        if (new_piece) {
+            // query rows of (b, g, rb), in registers for the whole piece; issued
+            // before the next loads so that waiting for them leaves those in flight
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) {
+                const int rr = rb * kRows + (wave * kNT + nt) * 32 + l32;
                 const bool valid = rr < a.S * a.G;
                 const int s = valid ? rr / a.G : 0, h = g * a.G + (valid ? rr % a.G : 0);
                 const uint16_t* q = a.Q + c.b * a.qsb + s * a.qss + h * a.qsh + hl * 8;
 #pragma unroll
                 for (int ds = 0; ds < C::DS; ++ds) {
-                    const u32x4 z = {0u, 0u, 0u, 0u};
-                    const u32x4 v = valid ? *reinterpret_cast<const u32x4*>(q + ds * 16) : z;
-                    qf[nt][ds] = __builtin_bit_cast(bf16x8, v);
+                    u32x4 v = *reinterpret_cast<const u32x4*>(q + ds * 16);
+                    if (!valid) v = u32x4{0u, 0u, 0u, 0u};
+                    st.qf[nt][ds] = __builtin_bit_cast(bf16x8, v);
                 }
-                m2[nt] = -INFINITY;
-                lsum[nt] = 0.f;
+            }
+        }
+        // refill this register set with tile u+2
+        if (ul < u1) {
+            load_tile<D>(R[S], cl, pg, a);
+            if (++ul < u1) {
+                advance(cl, a, ctx_len);
+                pg = tile_pages<D>(cl, a, page_table);
+            }
+        }
+        if (new_piece) {
+            st.piece_t0 = c.t;
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) {
+                st.m2[nt] = -INFINITY;
+                st.lsum[nt] = 0.f;
 #pragma unroll
                 for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) oacc[dt][nt][i] = 0.f;
+                    for (int i = 0; i < 16; ++i) st.oacc[dt][nt][i] = 0.f;
             }
         }
         const int nct = (c.L + kTile - 1) / kTile;
         const int nvalid = c.t < nct ? min(kTile, c.L - c.t * kTile) : a.S;
+        const uint8_t* Kst = stage;
+        const uint8_t* Vst = stage + C::TILEB;
 
-        // ---- scores: S^T[key][row] for 64 keys x 64 rows of this wave ----
-        const uint16_t* Ks = B;
-        const uint16_t* Vt = B + C::K_ELEMS;
-        f32x16 sacc[2][2];
+        // ---- scores: S^T[key][row] for 64 keys x 32*kNT rows of this wave ----
+        f32x16 sacc[2][kNT];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
+            for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) sacc[mt][nt][i] = 0.f;
+        // the two 32-key halves accumulate in alternation: independent MFMA chains
 #pragma unroll
         for (int ds = 0; ds < C::DS; ++ds) {
+            bf16x8 kf[2];
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                const bf16x8 kf = lds16(Ks + (mt * 32 + l32) * C::KSTR + ds * 16 + hl * 8);
+            for (int mt = 0; mt < 2; ++mt)
+                kf[mt] = lds16(Kst + (mt * 32 + l32) * C::ROWB + 16 * ((2 * ds + hl) ^ ksw));
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
-                    sacc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[nt][ds], sacc[mt][nt], 0, 0, 0);
-            }
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < kNT; ++nt)
+                    sacc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[mt], st.qf[nt][ds], sacc[mt][nt], 0, 0, 0);
         }
         if (nvalid < kTile) {
 #pragma unroll
@@ -337,16 +417,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a) {
                 for (int i = 0; i < 16; ++i) {
                     const int key = mt * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
                     if (key >= nvalid) {
-                        sacc[mt][0][i] = -INFINITY;
-                        sacc[mt][1][i] = -INFINITY;
+#pragma unroll
+                        for (int nt = 0; nt < kNT; ++nt) sacc[mt][nt][i] = -INFINITY;
                     }
                 }
         }
         // ---- online softmax (exp2 domain) ----
-        float mnew[2];
-        bool need[2];
+        float mnew[kNT];
+        bool need[kNT];
+        bool any_need = false;
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+        for (int nt = 0; nt < kNT; ++nt) {
             float mx = -INFINITY;
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
@@ -354,27 +435,28 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a) {
                 for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mt][nt][i]);
             mx = fmaxf(mx, __shfl_xor(mx, 32));
             mnew[nt] = mx * a.c_log2;
-            need[nt] = mnew[nt] > m2[nt] + kTau;
+            need[nt] = mnew[nt] > st.m2[nt] + kTau;
+            any_need = any_need || need[nt];
         }
-        if (__any(need[0] || need[1])) {
+        if (__any(any_need)) {
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
+            for (int nt = 0; nt < kNT; ++nt) {
                 float alpha = 1.f;
                 if (need[nt]) {
-                    alpha = __builtin_amdgcn_exp2f(m2[nt] - mnew[nt]);
-                    m2[nt] = mnew[nt];
+                    alpha = __builtin_amdgcn_exp2f(st.m2[nt] - mnew[nt]);
+                    st.m2[nt] = mnew[nt];
                 }
-                lsum[nt] *= alpha;
+                st.lsum[nt] *= alpha;
 #pragma unroll
                 for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) oacc[dt][nt][i] *= alpha;
+                    for (int i = 0; i < 16; ++i) st.oacc[dt][nt][i] *= alpha;
             }
         }
-        bf16x8 pf[4][2];
+        bf16x8 pf[4][kNT];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            const float neg = -m2[nt];
+        for (int nt = 0; nt < kNT; ++nt) {
+            const float neg = -st.m2[nt];
             float ls = 0.f;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
@@ -387,31 +469,41 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a) {
 #pragma unroll
                 for (int t = 0; t < 8; ++t) ls += (float)pb[t];
             }
-            lsum[nt] += ls;
+            st.lsum[nt] += ls;
         }
         // ---- O^T[d][row] += V^T . P^T ----
+        // V sits in LDS as [key][d]; the transposing read hands lane l the four keys
+        // kb..kb+3 of column d = 32*dt + l%32, with kb = 16*ks + 8*half + 4*(l/32):
+        // exactly the keys its P^T slots hold.
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
+            bf16x8 vf[C::DT];
 #pragma unroll
             for (int dt = 0; dt < C::DT; ++dt) {
-                const bf16x8 vf = lds16(Vt + (dt * 32 + l32) * C::VSTR + ks * 16 + hl * 8);
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
-                    oacc[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks][nt], oacc[dt][nt], 0, 0, 0);
+                const int cv = 4 * dt + vchunk;
+                const uint8_t* p0 = Vst + (ks * 16 + vrow) * C::ROWB + 16 * (cv ^ vsw0) + vbyte;
+                const uint8_t* p1 = Vst + (ks * 16 + vrow + 8) * C::ROWB + 16 * (cv ^ vsw1) + vbyte;
+                const i16x4 pair[2] = {lds_tr(p0), lds_tr(p1)};
+                vf[dt] = __builtin_bit_cast(bf16x8, pair);
             }
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+                for (int nt = 0; nt < kNT; ++nt)
+                    st.oacc[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dt], pf[ks][nt], st.oacc[dt][nt], 0, 0, 0);
         }
 
         // ---- end of piece: write the result or a partial ----
         if (c.t == c.units - 1 || u == u1 - 1) {
-            const bool full = piece_t0 == 0 && c.t == c.units - 1;
+            const bool full = st.piece_t0 == 0 && c.t == c.units - 1;
             const int p = c.b * mult + c.pl;
             const int slot = seg + p;
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                const float lt = lsum[nt] + __shfl_xor(lsum[nt], 32);
+            for (int nt = 0; nt < kNT; ++nt) {
+                const float lt = st.lsum[nt] + __shfl_xor(st.lsum[nt], 32);
                 const float inv = 1.f / lt;
-                const float lse = (m2[nt] + __log2f(lt)) * kLn2;
-                const int rl = wave * 64 + nt * 32 + l32;  // row within the block
+                const float lse = (st.m2[nt] + __log2f(lt)) * kLn2;
+                const int rl = (wave * kNT + nt) * 32 + l32;  // row within the block
                 const int rr = rb * kRows + rl;
                 if (rr >= a.S * a.G) continue;
                 if (full) {
@@ -422,8 +514,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a) {
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
                             const int d = dt * 32 + j * 8 + hl * 4;
-                            f32x4 o = {oacc[dt][nt][j * 4] * inv, oacc[dt][nt][j * 4 + 1] * inv,
-                                       oacc[dt][nt][j * 4 + 2] * inv, oacc[dt][nt][j * 4 + 3] * inv};
+                            f32x4 o = {st.oacc[dt][nt][j * 4] * inv, st.oacc[dt][nt][j * 4 + 1] * inv,
+                                       st.oacc[dt][nt][j * 4 + 2] * inv, st.oacc[dt][nt][j * 4 + 3] * inv};
                             if (a.o_f32) {
                                 *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.O) + ob + d) = o;
                             } else {
@@ -440,15 +532,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a) {
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
                             const int d = dt * 32 + j * 8 + hl * 4;
-                            f32x4 o = {oacc[dt][nt][j * 4] * inv, oacc[dt][nt][j * 4 + 1] * inv,
-                                       oacc[dt][nt][j * 4 + 2] * inv, oacc[dt][nt][j * 4 + 3] * inv};
+                            f32x4 o = {st.oacc[dt][nt][j * 4] * inv, st.oacc[dt][nt][j * 4 + 1] * inv,
+                                       st.oacc[dt][nt][j * 4 + 2] * inv, st.oacc[dt][nt][j * 4 + 3] * inv};
                             *reinterpret_cast<f32x4*>(po + d) = o;
                         }
                     if (hl == 0) a.part_lse[(long long)slot * kRows + rl] = lse;
                 }
             }
         }
-        buf ^= 1;
+        if (u + 1 < u1) advance(cc, a, ctx_len);
+    };
+
+    for (int u = u0; u < u1; u += 2) {
+        step(std::integral_constant<int, 0>{}, u);
+        if (u + 1 < u1) step(std::integral_constant<int, 1>{}, u + 1);
     }
 }
 
@@ -456,15 +553,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a) {
 // and write O = 0, LSE = -inf for pairs with no keys at all.
 // Grid: n_pairs * 16 workgroups of 256 threads, 16 rows each.
 template <int D>
-__global__ __launch_bounds__(kThreads) void attn_bf16_finalize(Args a) {
-    __shared__ int sh[260];
+__global__ __launch_bounds__(kFinThreads) void attn_bf16_finalize(Args a, const int* __restrict__ ctx_len) {
+    __shared__ int sh[kFinThreads + 4];
     const int mult = a.Hkv * a.n_rb;
     const int p = blockIdx.x / 16, chunk = blockIdx.x % 16;
     const int b = p / mult, pl = p % mult;
     const int g = pl / a.n_rb, rb = pl % a.n_rb;
     int W, bdummy, Cb;
-    scan_units(a, -1, b, sh, W, bdummy, Cb);
-    const int units = units_for(a, seq_len(a, b));
+    scan_units<kFinThreads>(a, ctx_len, -1, b, sh, W, bdummy, Cb);
+    const int units = units_for(a, seq_len(a, ctx_len, b));
     const int seg_len = (W + a.n_seg - 1) / a.n_seg;
     int s0 = 0, s1 = -1;
     if (units > 0) {
@@ -563,11 +660,11 @@ tt_status launch_attn_bf16(const tt_block_attn_params& p, const AttnPlan& pl, vo
     a.n_seg = pl.n_seg;
     a.c_log2 = p.softmax_scale * 1.44269504088896340736f;
     if (p.head_dim == 128) {
-        hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(pl.n_seg), dim3(kThreads), 0, s, a);
-        hipLaunchKernelGGL(attn_bf16_finalize<128>, dim3(pl.n_pairs * 16), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(pl.n_seg), dim3(kThreads), 0, s, a, a.page_table, a.ctx_len);
+        hipLaunchKernelGGL(attn_bf16_finalize<128>, dim3(pl.n_pairs * 16), dim3(kFinThreads), 0, s, a, a.ctx_len);
     } else {
-        hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(pl.n_seg), dim3(kThreads), 0, s, a);
-        hipLaunchKernelGGL(attn_bf16_finalize<64>, dim3(pl.n_pairs * 16), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(pl.n_seg), dim3(kThreads), 0, s, a, a.page_table, a.ctx_len);
+        hipLaunchKernelGGL(attn_bf16_finalize<64>, dim3(pl.n_pairs * 16), dim3(kFinThreads), 0, s, a, a.ctx_len);
     }
     return hipGetLastError() == hipSuccess ? TT_OK : TT_ERR_HIP;
 }

@@ -97,7 +97,7 @@ const char* tt_status_string(tt_status status);
  *   ctx_len    [B] int32 (device): prefix length per sequence, 0 allowed, any
  *              value (the last page may be partial). Values are clamped to
  *              [0, min(max_ctx_len, max_pages*page_size)]; a page id outside
- *              [0, num_pages) reads as zero keys (no fault, wrong result).
+ *              [0, num_pages) is clamped into it (no fault, wrong result).
  *   Kden, Vden [B][S][Hkv][head_dim] at base + b*den_stride_b + s*den_stride_s
  *              + g*den_stride_h; both NULL for a prefix-only partial.
  *   O          [B][S][Hq][head_dim] of o_dtype at O + b*o_stride_b + ...
