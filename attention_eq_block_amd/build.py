@@ -29,6 +29,9 @@ COMMON = [
     "-I", INCLUDE, "-I", CSRC,
     # no packed fp32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: the register allocator then keeps operands and
+    # prefetched tiles in AGPRs instead of spilling (attention kernel: 0 spills)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas",
 ]
 

@@ -40,8 +40,16 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 8;                 // waves per workgroup (two per SIMD)
-constexpr int kNT = kRows / (32 * kWaves); // 32-row MFMA tiles per wave
+#ifndef TT_ATTN_WAVES
+#define TT_ATTN_WAVES 8
+#endif
+#ifndef TT_ATTN_PREFETCH
+#define TT_ATTN_PREFETCH 2
+#endif
+constexpr int kWaves = TT_ATTN_WAVES;       // waves per workgroup; each owns kRows / kWaves query rows
+constexpr int kNT = kRows / (32 * kWaves);  // 32-row MFMA tiles per wave
+constexpr int kNR = TT_ATTN_PREFETCH;       // tiles in flight in registers (1 or 2)
+static_assert(kNT >= 1 && kNR >= 1 && kNR <= 2, "unsupported attention kernel shape");
 constexpr int kThreads = 64 * kWaves;
 constexpr int kFinThreads = 256;
 constexpr float kTau = 8.0f;  // lazy rescale threshold (log2 units)
@@ -56,7 +64,7 @@ struct Cfg {
     static constexpr int LPK = kTile * CPR / kThreads;  // 16-byte K (and V) loads per thread per tile
     static constexpr int DS = D / 16;              // k-steps of the score product
     static constexpr int DT = D / 32;              // d tiles of the output product
-    static_assert(LPK >= 1 && LPK <= 2, "one or two chunks of K and of V per thread and tile");
+    static_assert(LPK >= 1 && LPK <= 4, "up to four chunks of K and of V per thread and tile");
 };
 
 // Rows sit unpadded in LDS; the 16-byte chunk c of row r is stored at chunk
@@ -75,6 +83,7 @@ struct Args {
     const uint16_t* Kc;
     const uint16_t* Vc;
     int page_size, num_pages, max_pages, Lmax;
+    int page_shift;  // log2(page_size) when it is a power of two
     const int* page_table;
     const int* ctx_len;
     const uint16_t* Kd;
@@ -144,19 +153,44 @@ __device__ void scan_units(const Args& a, const int* __restrict__ ctx_len, int u
 struct Cur {
     int b, pl, t;    // sequence, pair index within the sequence (g*n_rb + rb), tile within the pair
     int L, units;    // prefix length, tiles per pair of sequence b
+    int nct;         // prefix tiles of sequence b
+    int g, rb;       // kv head and row block of pair pl
 };
+
+__device__ __forceinline__ void set_seq(Cur& c, const Args& a, const int* __restrict__ ctx_len, int b) {
+    c.b = b;
+    c.L = seq_len(a, ctx_len, b);
+    c.nct = (c.L + kTile - 1) / kTile;
+    c.units = c.nct + a.has_den;
+}
+
+__device__ __forceinline__ void set_pair(Cur& c, const Args& a, int pl) {
+    c.pl = pl;
+    c.g = pl / a.n_rb;
+    c.rb = pl - c.g * a.n_rb;
+}
 
 __device__ __forceinline__ void advance(Cur& c, const Args& a, const int* __restrict__ ctx_len) {
     if (++c.t < c.units) return;
     c.t = 0;
-    if (++c.pl < a.Hkv * a.n_rb) return;
-    c.pl = 0;
+    if (c.pl + 1 < a.Hkv * a.n_rb) {
+        set_pair(c, a, c.pl + 1);
+        return;
+    }
+    set_pair(c, a, 0);
     for (;;) {
-        if (++c.b >= a.B) { c.units = 1; return; }
-        c.L = seq_len(a, ctx_len, c.b);
-        c.units = units_for(a, c.L);
+        if (c.b + 1 >= a.B) { c.units = 1; return; }
+        set_seq(c, a, ctx_len, c.b + 1);
         if (c.units > 0) return;
     }
+}
+
+// j / page_size and j % page_size, by shifts when page_size is a power of two
+template <bool P2>
+__device__ __forceinline__ int page_of(const Args& a, int j) { return P2 ? (j >> a.page_shift) : j / a.page_size; }
+template <bool P2>
+__device__ __forceinline__ int slot_of(const Args& a, int j) {
+    return P2 ? (j & (a.page_size - 1)) : j % a.page_size;
 }
 
 __device__ __forceinline__ u32x4 ldg_nt(const uint16_t* p) {
@@ -175,21 +209,20 @@ struct Regs {
 };
 
 struct Pages {
-    int p[2];
+    int p[4];
 };
 
-template <int D>
+template <int D, bool P2>
 __device__ __forceinline__ Pages tile_pages(const Cur& c, const Args& a, const int* __restrict__ page_table) {
     using C = Cfg<D>;
-    Pages pg{{0, 0}};
-    const int nct = (c.L + kTile - 1) / kTile;
-    if (c.t >= nct) return pg;
+    Pages pg{{0, 0, 0, 0}};
+    if (c.t >= c.nct) return pg;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
     for (int i = 0; i < C::LPK; ++i) {
         const int r = (wave * 64 + kThreads * i) / C::CPR;  // first row of this wave's block
         const int j0 = min(c.t * kTile + r, c.L - 1);
-        pg.p[i] = page_table[(long long)c.b * a.max_pages + j0 / a.page_size];
+        pg.p[i] = page_table[(long long)c.b * a.max_pages + page_of<P2>(a, j0)];
     }
     return pg;
 }
@@ -199,30 +232,32 @@ __device__ __forceinline__ Pages tile_pages(const Cur& c, const Args& a, const i
 // a partial tile reads the tile's last valid key instead (finite, weight exactly
 // 0); a page id outside [0, num_pages) is clamped, so a corrupt table reads
 // wrong data but never faults.
-template <int D>
+template <int D, bool P2>
 __device__ __forceinline__ void load_tile(Regs<D>& r, const Cur& c, const Pages& pg, const Args& a) {
     using C = Cfg<D>;
-    const int tid = threadIdx.x;
-    const int g = c.pl / a.n_rb;
-    const int nct = (c.L + kTile - 1) / kTile;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ch = lane % C::CPR;       // 16-byte chunk of the row (64 is a multiple of CPR)
+    const int lrow = lane / C::CPR;     // row offset within this wave's block
 #pragma unroll
     for (int i = 0; i < C::LPK; ++i) {
-        const int q = tid + kThreads * i;
-        const int row = q / C::CPR, ch = q % C::CPR;
-        long long off;
+        const int rbase = (wave * 64 + kThreads * i) / C::CPR;  // uniform first row of the block
+        // wave-uniform base pointer plus a 32-bit per-lane element offset
         const uint16_t* kb;
         const uint16_t* vb;
-        if (c.t < nct) {
+        unsigned off;
+        if (c.t < c.nct) {
             const int page = min(max(pg.p[i], 0), a.num_pages - 1);
-            const int j = min(c.t * kTile + row, c.L - 1);
-            off = (((long long)page * a.Hkv + g) * a.page_size + j % a.page_size) * D + ch * 8;
-            kb = a.Kc;
-            vb = a.Vc;
+            const long long pbase = ((long long)page * a.Hkv + c.g) * a.page_size * D;
+            kb = a.Kc + pbase;
+            vb = a.Vc + pbase;
+            const int j = min(c.t * kTile + rbase + lrow, c.L - 1);
+            off = (unsigned)(slot_of<P2>(a, j) * D + ch * 8);
         } else {
-            const int j = min(row, a.S - 1);
-            off = (long long)c.b * a.dsb + (long long)j * a.dss + (long long)g * a.dsh + ch * 8;
-            kb = a.Kd;
-            vb = a.Vd;
+            const long long dbase = (long long)c.b * a.dsb + (long long)c.g * a.dsh;
+            kb = a.Kd + dbase;
+            vb = a.Vd + dbase;
+            off = (unsigned)(min(rbase + lrow, a.S - 1) * (int)a.dss + ch * 8);
         }
         r.k[i] = ldg_nt(kb + off);
         r.v[i] = ldg_nt(vb + off);
@@ -271,11 +306,12 @@ template <int D>
 struct State {
     bf16x8 qf[kNT][Cfg<D>::DS];
     f32x16 oacc[Cfg<D>::DT][kNT];
-    float m2[kNT], lsum[kNT];
+    f32x16 lacc[kNT];  // row sums of the rounded weights, from an MFMA against ones
+    float m2[kNT];
     int piece_t0;
 };
 
-template <int D>
+template <int D, bool P2>
 __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const int* __restrict__ page_table,
                                                                 const int* __restrict__ ctx_len) {
     using C = Cfg<D>;
@@ -302,32 +338,33 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
     c0 = __builtin_amdgcn_readfirstlane(c0);
 
     Cur cc;  // tile being computed
-    cc.b = b0;
-    cc.L = seq_len(a, ctx_len, b0);
-    cc.units = units_for(a, cc.L);
+    set_seq(cc, a, ctx_len, b0);
     {
         const int off = u0 - c0;
-        cc.pl = off / cc.units;
+        set_pair(cc, a, off / cc.units);
         cc.t = off % cc.units;
     }
     const int mult = a.Hkv * a.n_rb;
 
-    // Two register sets carry tiles u+1 and u+2 while tile u is computed: a tile's
-    // loads are issued two iterations before its registers are stored to LDS.
-    Regs<D> R[2];
+    // kNR register sets carry tiles u+1 .. u+kNR while tile u is computed: a tile's
+    // loads are issued kNR iterations before its registers are stored to LDS.
+    Regs<D> R[kNR];
     Cur cl = cc;  // next tile to load
     int ul = u0;
-    Pages pg = tile_pages<D>(cl, a, page_table);
+    Pages pg = tile_pages<D, P2>(cl, a, page_table);
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < kNR; ++k) {
         if (ul < u1) {
-            load_tile<D>(R[k], cl, pg, a);
+            load_tile<D, P2>(R[k], cl, pg, a);
             if (++ul < u1) {
                 advance(cl, a, ctx_len);
-                pg = tile_pages<D>(cl, a, page_table);
+                pg = tile_pages<D, P2>(cl, a, page_table);
             }
         }
     }
+    bf16x8 ones;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) ones[t] = (__bf16)1.0f;
 
     State<D> st;
     st.piece_t0 = 0;
@@ -342,10 +379,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
     auto step = [&](auto S_, int u) __attribute__((always_inline)) {
         constexpr int S = decltype(S_)::value;
         uint8_t* stage = smem + S * C::STAGEB;
-        store_tile<D>(R[S], stage);
+        store_tile<D>(R[S % kNR], stage);
         lds_barrier();
         const Cur c = cc;
-        const int g = c.pl / a.n_rb, rb = c.pl % a.n_rb;
+        const int g = c.g, rb = c.rb;
         const bool new_piece = u == u0 || c.t == 0;
         if (new_piece) {
             // query rows of (b, g, rb), in registers for the whole piece; issued
@@ -364,12 +401,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
                 }
             }
         }
-        // refill this register set with tile u+2
+        // refill this register set with tile u + kNR
         if (ul < u1) {
-            load_tile<D>(R[S], cl, pg, a);
+            load_tile<D, P2>(R[S % kNR], cl, pg, a);
             if (++ul < u1) {
                 advance(cl, a, ctx_len);
-                pg = tile_pages<D>(cl, a, page_table);
+                pg = tile_pages<D, P2>(cl, a, page_table);
             }
         }
         if (new_piece) {
@@ -377,15 +414,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
 #pragma unroll
             for (int nt = 0; nt < kNT; ++nt) {
                 st.m2[nt] = -INFINITY;
-                st.lsum[nt] = 0.f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) st.lacc[nt][i] = 0.f;
 #pragma unroll
                 for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) st.oacc[dt][nt][i] = 0.f;
             }
         }
-        const int nct = (c.L + kTile - 1) / kTile;
-        const int nvalid = c.t < nct ? min(kTile, c.L - c.t * kTile) : a.S;
+        const int nvalid = c.t < c.nct ? min(kTile, c.L - c.t * kTile) : a.S;
         const uint8_t* Kst = stage;
         const uint8_t* Vst = stage + C::TILEB;
 
@@ -409,6 +446,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
 #pragma unroll
                 for (int nt = 0; nt < kNT; ++nt)
                     sacc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[mt], st.qf[nt][ds], sacc[mt][nt], 0, 0, 0);
+            if (ds & 1) __builtin_amdgcn_sched_barrier(0);  // bound how far reads run ahead
         }
         if (nvalid < kTile) {
 #pragma unroll
@@ -422,6 +460,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
                     }
                 }
         }
+        __builtin_amdgcn_sched_barrier(0);
         // ---- online softmax (exp2 domain) ----
         float mnew[kNT];
         bool need[kNT];
@@ -446,7 +485,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
                     alpha = __builtin_amdgcn_exp2f(st.m2[nt] - mnew[nt]);
                     st.m2[nt] = mnew[nt];
                 }
-                st.lsum[nt] *= alpha;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) st.lacc[nt][i] *= alpha;
 #pragma unroll
                 for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
@@ -457,20 +497,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
             const float neg = -st.m2[nt];
-            float ls = 0.f;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 f32x8 pv;
 #pragma unroll
                 for (int t = 0; t < 8; ++t)
                     pv[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[ks >> 1][nt][(ks & 1) * 8 + t], a.c_log2, neg));
-                const bf16x8 pb = __builtin_convertvector(pv, bf16x8);
-                pf[ks][nt] = pb;
-#pragma unroll
-                for (int t = 0; t < 8; ++t) ls += (float)pb[t];
+                pf[ks][nt] = __builtin_convertvector(pv, bf16x8);
             }
-            st.lsum[nt] += ls;
         }
+        __builtin_amdgcn_sched_barrier(0);
         // ---- O^T[d][row] += V^T . P^T ----
         // V sits in LDS as [key][d]; the transposing read hands lane l the four keys
         // kb..kb+3 of column d = 32*dt + l%32, with kb = 16*ks + 8*half + 4*(l/32):
@@ -491,6 +527,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
 #pragma unroll
                 for (int nt = 0; nt < kNT; ++nt)
                     st.oacc[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dt], pf[ks][nt], st.oacc[dt][nt], 0, 0, 0);
+            // every row of ones . P^T is the row sum over these 16 keys
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt)
+                st.lacc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pf[ks][nt], st.lacc[nt], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
 
         // ---- end of piece: write the result or a partial ----
@@ -500,7 +541,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
             const int slot = seg + p;
 #pragma unroll
             for (int nt = 0; nt < kNT; ++nt) {
-                const float lt = st.lsum[nt] + __shfl_xor(st.lsum[nt], 32);
+                const float lt = st.lacc[nt][0];
                 const float inv = 1.f / lt;
                 const float lse = (st.m2[nt] + __log2f(lt)) * kLn2;
                 const int rl = (wave * kNT + nt) * 32 + l32;  // row within the block
@@ -561,7 +602,7 @@ __global__ __launch_bounds__(kFinThreads) void attn_bf16_finalize(Args a, const 
     const int g = pl / a.n_rb, rb = pl % a.n_rb;
     int W, bdummy, Cb;
     scan_units<kFinThreads>(a, ctx_len, -1, b, sh, W, bdummy, Cb);
-    const int units = units_for(a, seq_len(a, ctx_len, b));
+    const int units = units_for(a, seq_len(a, ctx_len, b));  // tiles per pair
     const int seg_len = (W + a.n_seg - 1) / a.n_seg;
     int s0 = 0, s1 = -1;
     if (units > 0) {
@@ -659,12 +700,21 @@ tt_status launch_attn_bf16(const tt_block_attn_params& p, const AttnPlan& pl, vo
     a.has_den = p.Kden ? 1 : 0;
     a.n_seg = pl.n_seg;
     a.c_log2 = p.softmax_scale * 1.44269504088896340736f;
+    a.page_shift = -1;
+    if (p.page_size > 0 && (p.page_size & (p.page_size - 1)) == 0) {
+        a.page_shift = 0;
+        while ((1 << a.page_shift) < p.page_size) ++a.page_shift;
+    }
+    const bool p2 = a.page_shift >= 0;
+    const dim3 grid(pl.n_seg), blk(kThreads), fgrid(pl.n_pairs * 16), fblk(kFinThreads);
     if (p.head_dim == 128) {
-        hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(pl.n_seg), dim3(kThreads), 0, s, a, a.page_table, a.ctx_len);
-        hipLaunchKernelGGL(attn_bf16_finalize<128>, dim3(pl.n_pairs * 16), dim3(kFinThreads), 0, s, a, a.ctx_len);
+        if (p2) hipLaunchKernelGGL((attn_bf16_kernel<128, true>), grid, blk, 0, s, a, a.page_table, a.ctx_len);
+        else hipLaunchKernelGGL((attn_bf16_kernel<128, false>), grid, blk, 0, s, a, a.page_table, a.ctx_len);
+        hipLaunchKernelGGL(attn_bf16_finalize<128>, fgrid, fblk, 0, s, a, a.ctx_len);
     } else {
-        hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(pl.n_seg), dim3(kThreads), 0, s, a, a.page_table, a.ctx_len);
-        hipLaunchKernelGGL(attn_bf16_finalize<64>, dim3(pl.n_pairs * 16), dim3(kFinThreads), 0, s, a, a.ctx_len);
+        if (p2) hipLaunchKernelGGL((attn_bf16_kernel<64, true>), grid, blk, 0, s, a, a.page_table, a.ctx_len);
+        else hipLaunchKernelGGL((attn_bf16_kernel<64, false>), grid, blk, 0, s, a, a.page_table, a.ctx_len);
+        hipLaunchKernelGGL(attn_bf16_finalize<64>, fgrid, fblk, 0, s, a, a.ctx_len);
     }
     return hipGetLastError() == hipSuccess ? TT_OK : TT_ERR_HIP;
 }
