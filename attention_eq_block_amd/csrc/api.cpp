@@ -37,8 +37,11 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 size_t esize(int dtype) { return dtype == TT_BF16 ? 2 : 4; }
 
-// strides (elements) of a head_dim-contiguous tensor must keep 16-byte alignment
-bool stride_ok(int64_t st, int dtype) { return st >= 0 && (st * (int64_t)esize(dtype)) % 16 == 0; }
+// strides (elements) of a head_dim-contiguous tensor must keep 16-byte alignment;
+// the kernels hold them in 32 bits
+bool stride_ok(int64_t st, int dtype) {
+    return st >= 0 && st < ((int64_t)1 << 31) && (st * (int64_t)esize(dtype)) % 16 == 0;
+}
 
 tt_status validate_attn(const tt_block_attn_params* p) {
     if (!p) return TT_ERR_NULL;
@@ -56,6 +59,7 @@ tt_status validate_attn(const tt_block_attn_params* p) {
         if (p->page_size < 16 || p->page_size % 16 != 0) return TT_ERR_SHAPE;
         if (p->num_pages < 1 || p->max_pages < 1) return TT_ERR_SHAPE;
         if ((int64_t)p->max_pages * p->page_size < p->max_ctx_len) return TT_ERR_SHAPE;
+        if ((int64_t)p->B * p->max_pages >= ((int64_t)1 << 30)) return TT_ERR_UNSUPPORTED;
         if (!aligned16(p->Kctx) || !aligned16(p->Vctx)) return TT_ERR_UNSUPPORTED;
     }
     if (!aligned16(p->Q) || !aligned16(p->O)) return TT_ERR_UNSUPPORTED;

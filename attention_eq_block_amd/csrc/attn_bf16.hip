@@ -26,6 +26,16 @@
 // (O normalised, LSE) per segment, merged by a second kernel. Segments are
 // numbered so that consecutive ones run on the same XCD, which keeps a pair's
 // partials in one L2.
+//
+// Schedule inside a workgroup (ping-pong). Eight waves own 32 query rows each
+// and form two groups of four, so that every SIMD runs one wave of each group.
+// Per tile a wave has a matrix phase (scores of tile i and the PV product of
+// tile i-1: MFMA and LDS reads) and a vector phase (softmax of tile i, the
+// staging of the next tile into LDS and the next global loads). Group 1 runs
+// one barrier interval behind group 0, so in every interval one wave on each
+// SIMD issues MFMAs while the other does vector work. Group 0 stages the K
+// half of every tile and group 1 the V half; each wave moves 16 keys of a
+// tile, so it needs one page id per tile.
 #include <type_traits>
 
 #include "tt_internal.h"
@@ -38,33 +48,25 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-#ifndef TT_ATTN_WAVES
-#define TT_ATTN_WAVES 8
-#endif
-#ifndef TT_ATTN_PREFETCH
-#define TT_ATTN_PREFETCH 2
-#endif
-constexpr int kWaves = TT_ATTN_WAVES;       // waves per workgroup; each owns kRows / kWaves query rows
-constexpr int kNT = kRows / (32 * kWaves);  // 32-row MFMA tiles per wave
-constexpr int kNR = TT_ATTN_PREFETCH;       // tiles in flight in registers (1 or 2)
-static_assert(kNT >= 1 && kNR >= 1 && kNR <= 2, "unsupported attention kernel shape");
+constexpr int kWaves = 8;                  // two groups of four waves, 32 query rows each
 constexpr int kThreads = 64 * kWaves;
 constexpr int kFinThreads = 256;
 constexpr float kTau = 8.0f;  // lazy rescale threshold (log2 units)
 constexpr float kLn2 = 0.693147180559945309f;
+static_assert(kRows == 32 * kWaves, "one 32-row MFMA tile per wave");
 
 template <int D>
 struct Cfg {
-    static constexpr int CPR = D / 8;              // 16-byte chunks per K/V row
-    static constexpr int ROWB = D * 2;             // bytes per row (rows are not padded)
-    static constexpr int TILEB = kTile * ROWB;     // bytes of one K (or V) tile
-    static constexpr int STAGEB = 2 * TILEB;       // K then V
-    static constexpr int LPK = kTile * CPR / kThreads;  // 16-byte K (and V) loads per thread per tile
-    static constexpr int DS = D / 16;              // k-steps of the score product
-    static constexpr int DT = D / 32;              // d tiles of the output product
-    static_assert(LPK >= 1 && LPK <= 4, "up to four chunks of K and of V per thread and tile");
+    static constexpr int CPR = D / 8;           // 16-byte chunks per K/V row
+    static constexpr int ROWB = D * 2;          // bytes per row (rows are not padded)
+    static constexpr int TILEB = kTile * ROWB;  // bytes of one K (or V) tile
+    static constexpr int RPI = 64 / CPR;        // rows one load instruction of a wave covers
+    static constexpr int LPG = 16 / RPI;        // load instructions per wave and tile (16 keys)
+    static constexpr int DS = D / 16;           // k-steps of the score product
+    static constexpr int DT = D / 32;           // d tiles of the output product
+    static_assert(LPG >= 1 && LPG <= 4, "");
 };
 
 // Rows sit unpadded in LDS; the 16-byte chunk c of row r is stored at chunk
@@ -77,9 +79,11 @@ __device__ __forceinline__ int swz(int r) {
     else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
+// Element strides are 32-bit here (the host layer checks that they fit), which
+// keeps the kernel's scalar state small.
 struct Args {
     const uint16_t* Q;
-    long long qsb, qss, qsh;
+    int qsb, qss, qsh;
     const uint16_t* Kc;
     const uint16_t* Vc;
     int page_size, num_pages, max_pages, Lmax;
@@ -88,9 +92,9 @@ struct Args {
     const int* ctx_len;
     const uint16_t* Kd;
     const uint16_t* Vd;
-    long long dsb, dss, dsh;
+    int dsb, dss, dsh;
     void* O;
-    long long osb, oss, osh;
+    int osb, oss, osh;
     int o_f32;
     float* LSE;
     float* part_o;
@@ -99,8 +103,11 @@ struct Args {
     float c_log2;  // softmax_scale * log2(e)
 };
 
+typedef __attribute__((address_space(4))) const int const_int;
+
+// ctx_len is read through the constant address space: scalar loads
 __device__ __forceinline__ int seq_len(const Args& a, const int* __restrict__ ctx_len, int b) {
-    return ctx_len ? clamp_len(ctx_len[b], a.Lmax) : 0;
+    return ctx_len ? clamp_len(((const_int*)ctx_len)[b], a.Lmax) : 0;
 }
 __device__ __forceinline__ int units_for(const Args& a, int L) { return (L + kTile - 1) / kTile + a.has_den; }
 
@@ -116,7 +123,7 @@ __device__ void scan_units(const Args& a, const int* __restrict__ ctx_len, int u
     const int lo = min(a.B, t * chunk), hi = min(a.B, lo + chunk);
     int sum = 0, before = 0;
     for (int b = lo; b < hi; ++b) {
-        const int n = units_for(a, seq_len(a, ctx_len, b)) * mult;
+        const int n = units_for(a, ctx_len ? clamp_len(ctx_len[b], a.Lmax) : 0) * mult;
         sum += n;
         if (b < b_prefix) before += n;
     }
@@ -137,7 +144,7 @@ __device__ void scan_units(const Args& a, const int* __restrict__ ctx_len, int u
     if (u >= 0 && u >= excl && u < incl) {
         int c = excl;
         for (int b = lo; b < hi; ++b) {
-            const int n = units_for(a, seq_len(a, ctx_len, b)) * mult;
+            const int n = units_for(a, ctx_len ? clamp_len(ctx_len[b], a.Lmax) : 0) * mult;
             if (u < c + n) { sh[NTHR] = b; sh[NTHR + 1] = c; break; }
             c += n;
         }
@@ -150,24 +157,26 @@ __device__ void scan_units(const Args& a, const int* __restrict__ ctx_len, int u
     __syncthreads();
 }
 
+// Position in the tile stream. Pair pl of sequence b is (kv head g, row block
+// pl - g*n_rb); its tiles are the prefix tiles t < units - has_den, then the
+// block-key tile.
 struct Cur {
-    int b, pl, t;    // sequence, pair index within the sequence (g*n_rb + rb), tile within the pair
-    int L, units;    // prefix length, tiles per pair of sequence b
-    int nct;         // prefix tiles of sequence b
-    int g, rb;       // kv head and row block of pair pl
+    int b, pl, t;  // sequence, pair index within the sequence (g*n_rb + rb), tile within the pair
+    int L, units;  // prefix length, tiles per pair of sequence b
+    int g;         // kv head of pair pl
 };
+
+__device__ __forceinline__ bool is_prefix(const Cur& c, const Args& a) { return c.t < c.units - a.has_den; }
 
 __device__ __forceinline__ void set_seq(Cur& c, const Args& a, const int* __restrict__ ctx_len, int b) {
     c.b = b;
     c.L = seq_len(a, ctx_len, b);
-    c.nct = (c.L + kTile - 1) / kTile;
-    c.units = c.nct + a.has_den;
+    c.units = (c.L + kTile - 1) / kTile + a.has_den;
 }
 
 __device__ __forceinline__ void set_pair(Cur& c, const Args& a, int pl) {
     c.pl = pl;
     c.g = pl / a.n_rb;
-    c.rb = pl - c.g * a.n_rb;
 }
 
 __device__ __forceinline__ void advance(Cur& c, const Args& a, const int* __restrict__ ctx_len) {
@@ -197,85 +206,65 @@ __device__ __forceinline__ u32x4 ldg_nt(const uint16_t* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-// ---- tile loads: global -> registers -> LDS --------------------------------
-// Thread t moves chunk (t + kThreads*i) of each tile: row r = that / CPR, 16-byte
-// chunk c = that % CPR. The rows a wave touches for one i lie in one 16-aligned
-// group of keys, hence in one page, so the page id is wave-uniform (a scalar
-// load, issued one tile ahead of the loads that use it).
+// ---- tile staging: global -> registers -> LDS ------------------------------
+// Wave w (0..3 within its group) moves keys 16w .. 16w+15 of its group's half
+// tile: load instruction i covers rows 16w + RPI*i + lane/CPR, 16-byte chunk
+// lane%CPR. Sixteen 16-aligned keys lie in one page, so one page id serves the
+// wave for the whole tile.
 template <int D>
 struct Regs {
-    u32x4 k[Cfg<D>::LPK];
-    u32x4 v[Cfg<D>::LPK];
+    u32x4 x[Cfg<D>::LPG];
 };
 
-struct Pages {
-    int p[4];
-};
-
-template <int D, bool P2>
-__device__ __forceinline__ Pages tile_pages(const Cur& c, const Args& a, const int* __restrict__ page_table) {
-    using C = Cfg<D>;
-    Pages pg{{0, 0, 0, 0}};
-    if (c.t >= c.nct) return pg;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-#pragma unroll
-    for (int i = 0; i < C::LPK; ++i) {
-        const int r = (wave * 64 + kThreads * i) / C::CPR;  // first row of this wave's block
-        const int j0 = min(c.t * kTile + r, c.L - 1);
-        pg.p[i] = page_table[(long long)c.b * a.max_pages + page_of<P2>(a, j0)];
-    }
-    return pg;
+// index into the page table of the page holding this wave's keys of tile c
+// (any valid index for the block-key tile, which reads no page)
+template <bool P2>
+__device__ __forceinline__ int page_index(const Cur& c, const Args& a, int wq) {
+    if (!is_prefix(c, a)) return 0;
+    const int j0 = min(c.t * kTile + 16 * wq, c.L - 1);
+    return c.b * a.max_pages + page_of<P2>(a, j0);
 }
 
-// Issue this thread's loads of the tile at c. Loads are unconditional and their
+// Issue this wave's loads of tile c. Loads are unconditional and their
 // registers are not touched until they are stored to LDS: a key past the end of
 // a partial tile reads the tile's last valid key instead (finite, weight exactly
 // 0); a page id outside [0, num_pages) is clamped, so a corrupt table reads
 // wrong data but never faults.
 template <int D, bool P2>
-__device__ __forceinline__ void load_tile(Regs<D>& r, const Cur& c, const Pages& pg, const Args& a) {
+__device__ __forceinline__ void load_tile(Regs<D>& r, const Cur& c, int page, const uint16_t* src_c,
+                                          const uint16_t* src_d, const Args& a, int wq, int lane) {
     using C = Cfg<D>;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int ch = lane % C::CPR;       // 16-byte chunk of the row (64 is a multiple of CPR)
-    const int lrow = lane / C::CPR;     // row offset within this wave's block
+    const int ch = lane % C::CPR;
+    const int lrow = lane / C::CPR;
+    const uint16_t* base;
+    unsigned off[C::LPG];
+    if (is_prefix(c, a)) {
+        page = min(max(page, 0), a.num_pages - 1);
+        base = src_c + ((long long)page * a.Hkv + c.g) * a.page_size * D;
 #pragma unroll
-    for (int i = 0; i < C::LPK; ++i) {
-        const int rbase = (wave * 64 + kThreads * i) / C::CPR;  // uniform first row of the block
-        // wave-uniform base pointer plus a 32-bit per-lane element offset
-        const uint16_t* kb;
-        const uint16_t* vb;
-        unsigned off;
-        if (c.t < c.nct) {
-            const int page = min(max(pg.p[i], 0), a.num_pages - 1);
-            const long long pbase = ((long long)page * a.Hkv + c.g) * a.page_size * D;
-            kb = a.Kc + pbase;
-            vb = a.Vc + pbase;
-            const int j = min(c.t * kTile + rbase + lrow, c.L - 1);
-            off = (unsigned)(slot_of<P2>(a, j) * D + ch * 8);
-        } else {
-            const long long dbase = (long long)c.b * a.dsb + (long long)c.g * a.dsh;
-            kb = a.Kd + dbase;
-            vb = a.Vd + dbase;
-            off = (unsigned)(min(rbase + lrow, a.S - 1) * (int)a.dss + ch * 8);
+        for (int i = 0; i < C::LPG; ++i) {
+            const int j = min(c.t * kTile + 16 * wq + C::RPI * i + lrow, c.L - 1);
+            off[i] = (unsigned)(slot_of<P2>(a, j) * D + ch * 8);
         }
-        r.k[i] = ldg_nt(kb + off);
-        r.v[i] = ldg_nt(vb + off);
+    } else {
+        base = src_d + (long long)c.b * a.dsb + (long long)c.g * a.dsh;
+#pragma unroll
+        for (int i = 0; i < C::LPG; ++i)
+            off[i] = (unsigned)(min(16 * wq + C::RPI * i + lrow, a.S - 1) * a.dss + ch * 8);
     }
+#pragma unroll
+    for (int i = 0; i < C::LPG; ++i) r.x[i] = ldg_nt(base + off[i]);
 }
 
-// registers -> LDS stage, chunk c of row r at chunk position c ^ swz(r)
+// registers -> LDS half tile, chunk c of row r at chunk position c ^ swz(r)
 template <int D>
-__device__ __forceinline__ void store_tile(const Regs<D>& r, uint8_t* stage) {
+__device__ __forceinline__ void store_tile(const Regs<D>& r, uint8_t* buf, int wq, int lane) {
     using C = Cfg<D>;
-    const int tid = threadIdx.x;
+    const int ch = lane % C::CPR;
 #pragma unroll
-    for (int i = 0; i < C::LPK; ++i) {
-        const int q = tid + kThreads * i;
-        const int row = q / C::CPR, ch = q % C::CPR;
-        const int off = row * C::ROWB + 16 * (ch ^ swz<D>(row));
-        *reinterpret_cast<u32x4*>(stage + off) = r.k[i];
-        *reinterpret_cast<u32x4*>(stage + C::TILEB + off) = r.v[i];
+    for (int i = 0; i < C::LPG; ++i) {
+        const int row = 16 * wq + C::RPI * i + lane / C::CPR;
+        *reinterpret_cast<u32x4*>(buf + row * C::ROWB + 16 * (ch ^ swz<D>(row))) = r.x[i];
     }
 }
 
@@ -292,8 +281,6 @@ __device__ __forceinline__ bf16x8 lds16(const uint8_t* p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-
 // Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes, lane i
 // receives element i%4 of the 8-byte rows read by lanes i/4, i/4+4, i/4+8, i/4+12.
 __device__ __forceinline__ i16x4 lds_tr(const uint8_t* p) {
@@ -301,25 +288,41 @@ __device__ __forceinline__ i16x4 lds_tr(const uint8_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
 }
 
-// Per-wave state carried across tiles.
-template <int D>
-struct State {
-    bf16x8 qf[kNT][Cfg<D>::DS];
-    f32x16 oacc[Cfg<D>::DT][kNT];
-    f32x16 lacc[kNT];  // row sums of the rounded weights, from an MFMA against ones
-    float m2[kNT];
-    int piece_t0;
-};
+// (x of this lane, x of lane l ^ 32), in some order: v_permlane32_swap
+// exchanges the upper 32 lanes of its first operand with the lower 32 lanes of
+// its second, so with x in both each lane ends up holding both values. Written
+// in assembly because the compiler's model of the builtin's second result is
+// wrong (it reads both results from one register). The s_nop pairs give the
+// wait states a VALU write needs before a permlane reads it, and after.
+__device__ __forceinline__ void with_partner(float x, float& p0, float& p1) {
+    unsigned a = __builtin_bit_cast(unsigned, x), b = a;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+    p0 = __builtin_bit_cast(float, a);
+    p1 = __builtin_bit_cast(float, b);
+}
+__device__ __forceinline__ float max_with_partner(float x) {
+    float p0, p1;
+    with_partner(x, p0, p1);
+    return fmaxf(p0, p1);
+}
+__device__ __forceinline__ float sum_with_partner(float x) {
+    float p0, p1;
+    with_partner(x, p0, p1);
+    return p0 + p1;
+}
 
 template <int D, bool P2>
 __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const int* __restrict__ page_table,
                                                                 const int* __restrict__ ctx_len) {
     using C = Cfg<D>;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * C::STAGEB];
+    // K tiles (two buffers), then V tiles (two buffers)
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * C::TILEB];
     __shared__ int sh[kThreads + 4];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2, wq = wave & 3;
     const int l32 = lane & 31, hl = lane >> 5;
 
     // logical segment of this workgroup: consecutive segments share an XCD
@@ -328,11 +331,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
 
     int W, b0, c0;
     scan_units<kThreads>(a, ctx_len, -1, -1, sh, W, b0, c0);  // total units W
-    W = __builtin_amdgcn_readfirstlane(W);                     // uniform: keep the walk in scalar registers
+    W = __builtin_amdgcn_readfirstlane(W);
     const int seg_len = (W + a.n_seg - 1) / a.n_seg;
     const int u0 = seg * seg_len;
-    const int u1 = min(W, u0 + seg_len);
-    if (u0 >= u1) return;
+    const int n = min(W, u0 + seg_len) - u0;  // tiles of this segment
+    if (n <= 0) return;
     scan_units<kThreads>(a, ctx_len, u0, -1, sh, W, b0, c0);
     b0 = __builtin_amdgcn_readfirstlane(b0);
     c0 = __builtin_amdgcn_readfirstlane(c0);
@@ -346,248 +349,284 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
     }
     const int mult = a.Hkv * a.n_rb;
 
-    // kNR register sets carry tiles u+1 .. u+kNR while tile u is computed: a tile's
-    // loads are issued kNR iterations before its registers are stored to LDS.
-    Regs<D> R[kNR];
-    Cur cl = cc;  // next tile to load
-    int ul = u0;
-    Pages pg = tile_pages<D, P2>(cl, a, page_table);
-#pragma unroll
-    for (int k = 0; k < kNR; ++k) {
-        if (ul < u1) {
-            load_tile<D, P2>(R[k], cl, pg, a);
-            if (++ul < u1) {
-                advance(cl, a, ctx_len);
-                pg = tile_pages<D, P2>(cl, a, page_table);
-            }
-        }
-    }
-    bf16x8 ones;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) ones[t] = (__bf16)1.0f;
+    // ---- this group's half of every tile ----
+    const uint16_t* src_c = grp ? a.Vc : a.Kc;
+    const uint16_t* src_d = grp ? a.Vd : a.Kd;
+    uint8_t* const mybuf = smem + grp * 2 * C::TILEB;
+    const uint8_t* const Kbuf = smem;
+    const uint8_t* const Vbuf = smem + 2 * C::TILEB;
+    // page ids through a bounds-checked buffer resource (an empty table reads 0)
+    const __amdgpu_buffer_rsrc_t ptab = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)page_table, (short)0, page_table ? a.B * a.max_pages * 4 : 0, 0x00020000);
 
-    State<D> st;
-    st.piece_t0 = 0;
-    // lane-constant parts of the swizzled LDS addresses
-    const int ksw = swz<D>(l32);
+    // Load pipeline: tile j's registers are filled two feeds before they are
+    // stored, and its page id one feed before that. Every feed issues the same
+    // loads (past the segment's end it reloads the last tile), so the wait
+    // counts the compiler derives are exact and never drain the pipeline.
+    Regs<D> R[2];
+    Cur cl = cc;  // next tile to load
+    int ul = 0;   // its index in the segment
+    int pg_cur = __builtin_amdgcn_raw_buffer_load_b32(ptab, page_index<P2>(cl, a, wq) * 4, 0, 0);
+    auto issue = [&](Regs<D>& r) __attribute__((always_inline)) {
+        Cur nx = cl;
+        if (ul + 1 < n) advance(nx, a, ctx_len);
+        const int pg_next = __builtin_amdgcn_raw_buffer_load_b32(ptab, page_index<P2>(nx, a, wq) * 4, 0, 0);
+        load_tile<D, P2>(r, cl, __builtin_amdgcn_readfirstlane(pg_cur), src_c, src_d, a, wq, lane);
+        pg_cur = pg_next;
+        cl = nx;
+        if (ul + 1 < n) ++ul;
+    };
+    issue(R[0]);
+    issue(R[1]);
+    // store tile j (if it exists) from R[j % 2] and refill that set with tile j + 2
+    auto feed = [&](auto J_, int j) __attribute__((always_inline)) {
+        constexpr int J = decltype(J_)::value;
+        if (j < n) store_tile<D>(R[J], mybuf + J * C::TILEB, wq, lane);
+        issue(R[J]);
+    };
+
+    // ---- per-wave state ----
+    bf16x8 qf[C::DS];
+    f32x16 oacc[C::DT];
+    f32x16 sacc[2];
+    bf16x8 pf[4];
+    float m2 = -INFINITY, lsum = 0.f;
+    int piece_t0 = 0;
+    // Lane-constant parts of the swizzled LDS addresses. Chunk (2*ds + hl) of
+    // row l32 sits at 16 * ((2*ds + hl) ^ swz(l32)) = 16 * (hl ^ swz(l32)) ^ 32*ds
+    // within the 256-byte-aligned row, so every score read is one per-lane
+    // offset XOR a per-step constant. Likewise the V reads: chunk 4*dt + vchunk
+    // of row vrow sits at 16 * (vchunk ^ swz(vrow)) ^ 64*dt.
     const int vrow = 4 * hl + ((lane & 15) >> 2);
-    const int vsw0 = swz<D>(vrow), vsw1 = swz<D>(vrow + 8);
     const int vchunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
     const int vbyte = 8 * (lane & 1);
+    const int kaddr = l32 * C::ROWB + 16 * (hl ^ swz<D>(l32));
+    const int vaddr0 = vrow * C::ROWB + 16 * (vchunk ^ swz<D>(vrow)) + vbyte;
+    const int vaddr1 = (vrow + 8) * C::ROWB + 16 * (vchunk ^ swz<D>(vrow + 8)) + vbyte;
 
-    // one tile; S is the register set / LDS stage of tile u (u - u0 even: 0)
-    auto step = [&](auto S_, int u) __attribute__((always_inline)) {
-        constexpr int S = decltype(S_)::value;
-        uint8_t* stage = smem + S * C::STAGEB;
-        store_tile<D>(R[S % kNR], stage);
-        lds_barrier();
-        const Cur c = cc;
-        const int g = c.g, rb = c.rb;
-        const bool new_piece = u == u0 || c.t == 0;
-        if (new_piece) {
-            // query rows of (b, g, rb), in registers for the whole piece; issued
-            // before the next loads so that waiting for them leaves those in flight
+    // query rows of the pair at c (a row past S*G reads the last row; it is never written)
+    auto load_q = [&](const Cur& c) __attribute__((always_inline)) {
+        const int rb = c.pl - c.g * a.n_rb;
+        const int rr = min(rb * kRows + wave * 32 + l32, a.S * a.G - 1);
+        const int s = rr / a.G, h = c.g * a.G + rr % a.G;
+        const uint16_t* q = a.Q + (long long)c.b * a.qsb + (long long)s * a.qss + (long long)h * a.qsh + hl * 8;
 #pragma unroll
-            for (int nt = 0; nt < kNT; ++nt) {
-                const int rr = rb * kRows + (wave * kNT + nt) * 32 + l32;
-                const bool valid = rr < a.S * a.G;
-                const int s = valid ? rr / a.G : 0, h = g * a.G + (valid ? rr % a.G : 0);
-                const uint16_t* q = a.Q + c.b * a.qsb + s * a.qss + h * a.qsh + hl * 8;
-#pragma unroll
-                for (int ds = 0; ds < C::DS; ++ds) {
-                    u32x4 v = *reinterpret_cast<const u32x4*>(q + ds * 16);
-                    if (!valid) v = u32x4{0u, 0u, 0u, 0u};
-                    st.qf[nt][ds] = __builtin_bit_cast(bf16x8, v);
-                }
-            }
-        }
-        // refill this register set with tile u + kNR
-        if (ul < u1) {
-            load_tile<D, P2>(R[S % kNR], cl, pg, a);
-            if (++ul < u1) {
-                advance(cl, a, ctx_len);
-                pg = tile_pages<D, P2>(cl, a, page_table);
-            }
-        }
-        if (new_piece) {
-            st.piece_t0 = c.t;
-#pragma unroll
-            for (int nt = 0; nt < kNT; ++nt) {
-                st.m2[nt] = -INFINITY;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) st.lacc[nt][i] = 0.f;
-#pragma unroll
-                for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) st.oacc[dt][nt][i] = 0.f;
-            }
-        }
-        const int nvalid = c.t < c.nct ? min(kTile, c.L - c.t * kTile) : a.S;
-        const uint8_t* Kst = stage;
-        const uint8_t* Vst = stage + C::TILEB;
+        for (int ds = 0; ds < C::DS; ++ds) qf[ds] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q + ds * 16));
+    };
 
-        // ---- scores: S^T[key][row] for 64 keys x 32*kNT rows of this wave ----
-        f32x16 sacc[2][kNT];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < kNT; ++nt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) sacc[mt][nt][i] = 0.f;
-        // the two 32-key halves accumulate in alternation: independent MFMA chains
-#pragma unroll
-        for (int ds = 0; ds < C::DS; ++ds) {
-            bf16x8 kf[2];
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-                kf[mt] = lds16(Kst + (mt * 32 + l32) * C::ROWB + 16 * ((2 * ds + hl) ^ ksw));
+    // matrix phase: S^T of the tile in K buffer KB (if QK), then O^T += V^T P^T
+    // for the previous tile, in V buffer VB (if PV); the two chains interleave
+    auto matrix = [&](auto QK_, auto PV_, auto KB_, auto VB_) __attribute__((always_inline)) {
+        constexpr bool QK = decltype(QK_)::value;
+        constexpr bool PV = decltype(PV_)::value;
+        const uint8_t* Kst = Kbuf + decltype(KB_)::value * C::TILEB;
+        const uint8_t* Vst = Vbuf + decltype(VB_)::value * C::TILEB;
+        __builtin_amdgcn_s_setprio(1);
+        if constexpr (QK) {
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                for (int nt = 0; nt < kNT; ++nt)
-                    sacc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[mt], st.qf[nt][ds], sacc[mt][nt], 0, 0, 0);
-            if (ds & 1) __builtin_amdgcn_sched_barrier(0);  // bound how far reads run ahead
+                for (int e = 0; e < 16; ++e) sacc[mt][e] = 0.f;
         }
-        if (nvalid < kTile) {
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = mt * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
-                    if (key >= nvalid) {
-#pragma unroll
-                        for (int nt = 0; nt < kNT; ++nt) sacc[mt][nt][i] = -INFINITY;
-                    }
-                }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        // ---- online softmax (exp2 domain) ----
-        float mnew[kNT];
-        bool need[kNT];
-        bool any_need = false;
-#pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) {
-            float mx = -INFINITY;
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mt][nt][i]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            mnew[nt] = mx * a.c_log2;
-            need[nt] = mnew[nt] > st.m2[nt] + kTau;
-            any_need = any_need || need[nt];
-        }
-        if (__any(any_need)) {
-#pragma unroll
-            for (int nt = 0; nt < kNT; ++nt) {
-                float alpha = 1.f;
-                if (need[nt]) {
-                    alpha = __builtin_amdgcn_exp2f(st.m2[nt] - mnew[nt]);
-                    st.m2[nt] = mnew[nt];
-                }
-#pragma unroll
-                for (int i = 0; i < 16; ++i) st.lacc[nt][i] *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) st.oacc[dt][nt][i] *= alpha;
-            }
-        }
-        bf16x8 pf[4][kNT];
-#pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) {
-            const float neg = -st.m2[nt];
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                f32x8 pv;
-#pragma unroll
-                for (int t = 0; t < 8; ++t)
-                    pv[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[ks >> 1][nt][(ks & 1) * 8 + t], a.c_log2, neg));
-                pf[ks][nt] = __builtin_convertvector(pv, bf16x8);
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        // ---- O^T[d][row] += V^T . P^T ----
-        // V sits in LDS as [key][d]; the transposing read hands lane l the four keys
-        // kb..kb+3 of column d = 32*dt + l%32, with kb = 16*ks + 8*half + 4*(l/32):
-        // exactly the keys its P^T slots hold.
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            bf16x8 vf[C::DT];
+            if constexpr (QK) {
 #pragma unroll
-            for (int dt = 0; dt < C::DT; ++dt) {
-                const int cv = 4 * dt + vchunk;
-                const uint8_t* p0 = Vst + (ks * 16 + vrow) * C::ROWB + 16 * (cv ^ vsw0) + vbyte;
-                const uint8_t* p1 = Vst + (ks * 16 + vrow + 8) * C::ROWB + 16 * (cv ^ vsw1) + vbyte;
-                const i16x4 pair[2] = {lds_tr(p0), lds_tr(p1)};
-                vf[dt] = __builtin_bit_cast(bf16x8, pair);
+                for (int dd = 0; dd < C::DS / 4; ++dd) {
+                    const int ds = ks * (C::DS / 4) + dd;
+                    bf16x8 kf[2];
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt)
+                        kf[mt] = lds16(Kst + (kaddr ^ (32 * ds)) + mt * 32 * C::ROWB);
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt)
+                        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[mt], qf[ds], sacc[mt], 0, 0, 0);
+                }
             }
+            if constexpr (PV) {
+                // V sits in LDS as [key][d]; the transposing read hands lane l the four keys
+                // kb..kb+3 of column d = 32*dt + l%32, with kb = 16*ks + 8*half + 4*(l/32):
+                // exactly the keys its P^T slots hold.
+                bf16x8 vf[C::DT];
+#pragma unroll
+                for (int dt = 0; dt < C::DT; ++dt) {
+                    const uint8_t* p0 = Vst + (vaddr0 ^ (64 * dt)) + ks * 16 * C::ROWB;
+                    const uint8_t* p1 = Vst + (vaddr1 ^ (64 * dt)) + ks * 16 * C::ROWB;
+                    const i16x4 pair[2] = {lds_tr(p0), lds_tr(p1)};
+                    vf[dt] = __builtin_bit_cast(bf16x8, pair);
+                }
+#pragma unroll
+                for (int dt = 0; dt < C::DT; ++dt)
+                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dt], pf[ks], oacc[dt], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // A finished piece of pair pl of sequence b: the normalised output if the
+    // piece is the whole pair, else a partial for the merge kernel. oacc is
+    // scaled in place (the caller resets it next).
+    auto epilogue = [&](int b, int pl, int g, bool full) __attribute__((always_inline)) {
+        const float lt = sum_with_partner(lsum);
+        const float inv = 1.f / lt;
+        const float lse = (m2 + __log2f(lt)) * kLn2;
+        const int rl = wave * 32 + l32;  // row within the block
+        const int rr = (pl - g * a.n_rb) * kRows + rl;
+        if (rr >= a.S * a.G) return;
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) oacc[dt][e] *= inv;
+        // lane holds d = 32*dt + 8*j + 4*hl + (0..3) in oacc[dt][4j .. 4j+3]
+        if (full) {
+            const int s = rr / a.G, h = g * a.G + rr % a.G;
+            const long long ob = (long long)b * a.osb + (long long)s * a.oss + (long long)h * a.osh + hl * 4;
+            if (a.o_f32) {
+                float* o = reinterpret_cast<float*>(a.O) + ob;
+#pragma unroll
+                for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        *reinterpret_cast<f32x4*>(o + dt * 32 + j * 8) =
+                            f32x4{oacc[dt][4 * j], oacc[dt][4 * j + 1], oacc[dt][4 * j + 2], oacc[dt][4 * j + 3]};
+            } else {
+                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                __bf16* o = reinterpret_cast<__bf16*>(a.O) + ob;
+#pragma unroll
+                for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        *reinterpret_cast<bf16x4*>(o + dt * 32 + j * 8) = __builtin_convertvector(
+                            (f32x4{oacc[dt][4 * j], oacc[dt][4 * j + 1], oacc[dt][4 * j + 2], oacc[dt][4 * j + 3]}),
+                            bf16x4);
+            }
+            if (a.LSE && hl == 0) a.LSE[((long long)b * a.Hq + h) * a.S + s] = lse;
+        } else {
+            const long long slot = seg + b * mult + pl;
+            float* po = a.part_o + (slot * kRows + rl) * D + hl * 4;
 #pragma unroll
             for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-                for (int nt = 0; nt < kNT; ++nt)
-                    st.oacc[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dt], pf[ks][nt], st.oacc[dt][nt], 0, 0, 0);
-            // every row of ones . P^T is the row sum over these 16 keys
-#pragma unroll
-            for (int nt = 0; nt < kNT; ++nt)
-                st.lacc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pf[ks][nt], st.lacc[nt], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
+                for (int j = 0; j < 4; ++j)
+                    *reinterpret_cast<f32x4*>(po + dt * 32 + j * 8) =
+                        f32x4{oacc[dt][4 * j], oacc[dt][4 * j + 1], oacc[dt][4 * j + 2], oacc[dt][4 * j + 3]};
+            if (hl == 0) a.part_lse[slot * kRows + rl] = lse;
         }
-
-        // ---- end of piece: write the result or a partial ----
-        if (c.t == c.units - 1 || u == u1 - 1) {
-            const bool full = st.piece_t0 == 0 && c.t == c.units - 1;
-            const int p = c.b * mult + c.pl;
-            const int slot = seg + p;
-#pragma unroll
-            for (int nt = 0; nt < kNT; ++nt) {
-                const float lt = st.lacc[nt][0];
-                const float inv = 1.f / lt;
-                const float lse = (st.m2[nt] + __log2f(lt)) * kLn2;
-                const int rl = (wave * kNT + nt) * 32 + l32;  // row within the block
-                const int rr = rb * kRows + rl;
-                if (rr >= a.S * a.G) continue;
-                if (full) {
-                    const int s = rr / a.G, h = g * a.G + rr % a.G;
-                    const long long ob = c.b * a.osb + s * a.oss + h * a.osh;
-#pragma unroll
-                    for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const int d = dt * 32 + j * 8 + hl * 4;
-                            f32x4 o = {st.oacc[dt][nt][j * 4] * inv, st.oacc[dt][nt][j * 4 + 1] * inv,
-                                       st.oacc[dt][nt][j * 4 + 2] * inv, st.oacc[dt][nt][j * 4 + 3] * inv};
-                            if (a.o_f32) {
-                                *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.O) + ob + d) = o;
-                            } else {
-                                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-                                const bf16x4 ob4 = __builtin_convertvector(o, bf16x4);
-                                *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(a.O) + ob + d) = ob4;
-                            }
-                        }
-                    if (a.LSE && hl == 0) a.LSE[((long long)c.b * a.Hq + h) * a.S + s] = lse;
-                } else {
-                    float* po = a.part_o + ((long long)slot * kRows + rl) * D;
-#pragma unroll
-                    for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const int d = dt * 32 + j * 8 + hl * 4;
-                            f32x4 o = {st.oacc[dt][nt][j * 4] * inv, st.oacc[dt][nt][j * 4 + 1] * inv,
-                                       st.oacc[dt][nt][j * 4 + 2] * inv, st.oacc[dt][nt][j * 4 + 3] * inv};
-                            *reinterpret_cast<f32x4*>(po + d) = o;
-                        }
-                    if (hl == 0) a.part_lse[(long long)slot * kRows + rl] = lse;
-                }
-            }
-        }
-        if (u + 1 < u1) advance(cc, a, ctx_len);
     };
 
-    for (int u = u0; u < u1; u += 2) {
-        step(std::integral_constant<int, 0>{}, u);
-        if (u + 1 < u1) step(std::integral_constant<int, 1>{}, u + 1);
+    // the piece of tile i - 1, if that tile ended its pair
+    bool prev_ends = false;
+    int prev_b = 0, prev_pl = 0, prev_g = 0;
+    // vector phase of tile i: close the piece that ended with tile i-1 (its last
+    // PV product ran in this tile's matrix phase), softmax of tile i, stage tile i+1
+    auto vector = [&](auto P_, int i) __attribute__((always_inline)) {
+        constexpr int P = decltype(P_)::value;  // i % 2
+        __builtin_amdgcn_s_setprio(0);
+        const bool close_prev = i > 0 && prev_ends;
+        if (close_prev) epilogue(prev_b, prev_pl, prev_g, piece_t0 == 0);
+        if (i == 0 || close_prev) {
+            piece_t0 = cc.t;
+            m2 = -INFINITY;
+            lsum = 0.f;
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) oacc[dt][e] = 0.f;
+        }
+        const int nvalid = is_prefix(cc, a) ? min(kTile, cc.L - cc.t * kTile) : a.S;
+        if (nvalid < kTile) {
+            // key of element e of sacc[mt] is mt*32 + 8*(e/4) + e%4 + 4*hl
+            const int lim = nvalid - 4 * hl;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    if (mt * 32 + (e >> 2) * 8 + (e & 3) >= lim) sacc[mt][e] = -INFINITY;
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[mt][e]);
+        const float mnew = max_with_partner(mx) * a.c_log2;
+        const bool need = mnew > m2 + kTau;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+            const float alpha = need ? __builtin_amdgcn_exp2f(m2 - mnew) : 1.f;
+            if (need) m2 = mnew;
+            lsum *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
+        }
+        const float neg = -m2;
+        float ls = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            f32x8 pv;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[ks >> 1][(ks & 1) * 8 + e], a.c_log2, neg));
+                ls += pv[e];
+            }
+            pf[ks] = __builtin_convertvector(pv, bf16x8);
+        }
+        lsum += ls;
+        // next tile: its query rows if it starts a new piece (issued before the
+        // staging loads, so waiting for them leaves those in flight), then staging
+        prev_ends = cc.t == cc.units - 1;
+        prev_b = cc.b;
+        prev_pl = cc.pl;
+        prev_g = cc.g;
+        if (i + 1 < n) {
+            advance(cc, a, ctx_len);
+            if (cc.t == 0) load_q(cc);
+        }
+        feed(std::integral_constant<int, 1 - P>{}, i + 1);
+    };
+
+    // ---- prologue: group 0 stages K of tile 0 before the first barrier, group 1
+    // stages V of tile 0 in the first interval ----
+    load_q(cc);
+    if (grp == 0) feed(std::integral_constant<int, 0>{}, 0);
+    lds_barrier();
+    if (grp == 1) {
+        feed(std::integral_constant<int, 0>{}, 0);
+        lds_barrier();
     }
+    using F = std::false_type;
+    using T = std::true_type;
+    using Z = std::integral_constant<int, 0>;
+    using O = std::integral_constant<int, 1>;
+    // Tile i: matrix(i) = scores of i (K buffer i%2) and PV of i-1 (V buffer
+    // (i-1)%2), then vector(i). The loop runs from one vector phase to the next.
+    matrix(T{}, F{}, Z{}, Z{});
+    lds_barrier();
+    int i = 0;
+    for (; i + 2 < n; i += 2) {
+        vector(Z{}, i);
+        lds_barrier();
+        matrix(T{}, T{}, O{}, Z{});
+        lds_barrier();
+        vector(O{}, i + 1);
+        lds_barrier();
+        matrix(T{}, T{}, Z{}, O{});
+        lds_barrier();
+    }
+    vector(Z{}, i);
+    lds_barrier();
+    if (i + 1 < n) {
+        matrix(T{}, T{}, O{}, Z{});
+        lds_barrier();
+        vector(O{}, i + 1);
+        lds_barrier();
+        matrix(F{}, T{}, Z{}, O{});  // PV of the last tile (odd)
+    } else {
+        matrix(F{}, T{}, Z{}, Z{});  // PV of the last tile (even)
+    }
+    __builtin_amdgcn_s_setprio(0);
+    epilogue(cc.b, cc.pl, cc.g, piece_t0 == 0 && cc.t == cc.units - 1);
+    if (grp == 0) lds_barrier();
 }
 
 // Merge the per-segment partials of every pair that segment boundaries cut,
@@ -602,7 +641,7 @@ __global__ __launch_bounds__(kFinThreads) void attn_bf16_finalize(Args a, const 
     const int g = pl / a.n_rb, rb = pl % a.n_rb;
     int W, bdummy, Cb;
     scan_units<kFinThreads>(a, ctx_len, -1, b, sh, W, bdummy, Cb);
-    const int units = units_for(a, seq_len(a, ctx_len, b));  // tiles per pair
+    const int units = units_for(a, ctx_len ? clamp_len(ctx_len[b], a.Lmax) : 0);  // tiles per pair
     const int seg_len = (W + a.n_seg - 1) / a.n_seg;
     int s0 = 0, s1 = -1;
     if (units > 0) {
@@ -616,7 +655,7 @@ __global__ __launch_bounds__(kFinThreads) void attn_bf16_finalize(Args a, const 
     const int rr = rb * kRows + rl;
     if (rr >= a.S * a.G) return;
     const int s = rr / a.G, h = g * a.G + rr % a.G;
-    const long long ob = b * a.osb + s * a.oss + h * a.osh;
+    const long long ob = (long long)b * a.osb + (long long)s * a.oss + (long long)h * a.osh;
     float M = -INFINITY;
     for (int sg = s0; sg <= s1; ++sg) M = fmaxf(M, a.part_lse[(long long)(sg + p) * kRows + rl]);
     constexpr int PER = D / 64;  // 4-float chunks per thread
@@ -677,19 +716,19 @@ AttnPlan plan_attn_bf16(const tt_block_attn_params& p, int n_cu) {
 tt_status launch_attn_bf16(const tt_block_attn_params& p, const AttnPlan& pl, void* ws, hipStream_t s) {
     Args a{};
     a.Q = static_cast<const uint16_t*>(p.Q);
-    a.qsb = p.q_stride_b; a.qss = p.q_stride_s; a.qsh = p.q_stride_h;
+    a.qsb = (int)p.q_stride_b; a.qss = (int)p.q_stride_s; a.qsh = (int)p.q_stride_h;
     a.Kc = static_cast<const uint16_t*>(p.Kctx);
     a.Vc = static_cast<const uint16_t*>(p.Vctx);
     a.page_size = p.page_size; a.num_pages = p.num_pages; a.max_pages = p.max_pages;
     const long long cap = (long long)p.max_pages * p.page_size;
     a.Lmax = (int)(p.max_ctx_len < cap ? p.max_ctx_len : cap);
-    a.page_table = p.page_table;
+    a.page_table = p.max_ctx_len > 0 ? p.page_table : nullptr;
     a.ctx_len = p.max_ctx_len > 0 ? p.ctx_len : nullptr;
     a.Kd = static_cast<const uint16_t*>(p.Kden);
     a.Vd = static_cast<const uint16_t*>(p.Vden);
-    a.dsb = p.den_stride_b; a.dss = p.den_stride_s; a.dsh = p.den_stride_h;
+    a.dsb = (int)p.den_stride_b; a.dss = (int)p.den_stride_s; a.dsh = (int)p.den_stride_h;
     a.O = p.O;
-    a.osb = p.o_stride_b; a.oss = p.o_stride_s; a.osh = p.o_stride_h;
+    a.osb = (int)p.o_stride_b; a.oss = (int)p.o_stride_s; a.osh = (int)p.o_stride_h;
     a.o_f32 = p.o_dtype == TT_F32;
     a.LSE = p.LSE;
     char* w = static_cast<char*>(ws);

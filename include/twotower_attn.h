@@ -107,7 +107,9 @@ const char* tt_status_string(tt_status status);
  *
  * Supported: dtype TT_BF16 (MFMA path, float32 accumulation) or TT_F32
  * (float32 path); head_dim 64 or 128; 1 <= S <= 64; Hq % Hkv == 0;
- * page_size a positive multiple of 16; softmax_scale finite and > 0.
+ * page_size a positive multiple of 16; softmax_scale finite and > 0; every
+ * element stride below 2^31 and B*max_pages below 2^30 (TT_ERR_UNSUPPORTED
+ * otherwise).
  */
 typedef struct tt_block_attn_params {
     int32_t dtype;        /* tt_dtype of Q and K/V */

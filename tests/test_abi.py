@@ -73,7 +73,9 @@ def call_attn(p, ws=None, nbytes=0):
     (dict(max_ctx_len=-3), 2),
     (dict(Q=FAKE + 8), 4), (dict(O=FAKE + 2), 4), (dict(Kctx=FAKE + 4), 4), (dict(q_stride_h=100), 4),
     (dict(den_stride_s=4), 4), (dict(o_stride_b=-8), 4),
-    (dict(B=1 << 22, max_ctx_len=1 << 20, max_pages=1 << 16), 2),
+    (dict(B=1 << 13, page_size=1024, max_ctx_len=1 << 26, max_pages=1 << 16), 2),  # 2^34 tiles
+    (dict(q_stride_b=1 << 31), 4), (dict(o_stride_s=1 << 32), 4),  # strides must fit 31 bits
+    (dict(B=1 << 15, max_pages=1 << 15), 4),  # page table past 2^30 entries
 ])
 def test_attn_validation(kw, code):
     rc = call_attn(attn_ok(**kw))
