@@ -50,7 +50,11 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
+#ifndef TT_ATTN_PREFETCH
+#define TT_ATTN_PREFETCH 2
+#endif
 constexpr int kWaves = 8;                  // two groups of four waves, 32 query rows each
+constexpr int kNR = TT_ATTN_PREFETCH;      // tiles in flight in registers per wave (1 or 2)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kFinThreads = 256;
 constexpr float kTau = 8.0f;  // lazy rescale threshold (log2 units)
@@ -60,8 +64,11 @@ static_assert(kRows == 32 * kWaves, "one 32-row MFMA tile per wave");
 template <int D>
 struct Cfg {
     static constexpr int CPR = D / 8;           // 16-byte chunks per K/V row
-    static constexpr int ROWB = D * 2;          // bytes per row (rows are not padded)
-    static constexpr int TILEB = kTile * ROWB;  // bytes of one K (or V) tile
+    static constexpr int ROWB = D * 2;          // bytes of one K/V row
+    static constexpr int KROW = ROWB + 16;      // LDS row pitch of K tiles
+    static constexpr int VROW = ROWB + 64;      // LDS row pitch of V tiles
+    static constexpr int KTILE = kTile * KROW;  // LDS bytes of one K tile
+    static constexpr int VTILE = kTile * VROW;  // LDS bytes of one V tile
     static constexpr int RPI = 64 / CPR;        // rows one load instruction of a wave covers
     static constexpr int LPG = 16 / RPI;        // load instructions per wave and tile (16 keys)
     static constexpr int DS = D / 16;           // k-steps of the score product
@@ -69,15 +76,13 @@ struct Cfg {
     static_assert(LPG >= 1 && LPG <= 4, "");
 };
 
-// Rows sit unpadded in LDS; the 16-byte chunk c of row r is stored at chunk
-// position c ^ swz(r). Over any 16 consecutive rows (the rows one 16-lane
-// phase of a K-operand read touches) and over the 4-row x 4-chunk blocks of a
-// transposing V read, the swizzle sends the accessed chunks to distinct banks.
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-}
+// LDS tiles keep the [key][d] layout with padded rows. A score-operand read
+// (ds_read_b128) has 16 lanes read one 16-byte chunk of 16 consecutive rows:
+// with a 272-byte K pitch (68 banks) those land on 16 disjoint 4-bank groups.
+// A transposing V read (ds_read_b64_tr_b16) has 32 lanes read 64 contiguous
+// bytes of each of 4 consecutive rows: with a 320-byte V pitch (80 banks)
+// those are 4 disjoint 16-bank groups. The padding keeps every address a
+// per-lane base plus a compile-time offset.
 
 // Element strides are 32-bit here (the host layer checks that they fit), which
 // keeps the kernel's scalar state small.
@@ -216,15 +221,6 @@ struct Regs {
     u32x4 x[Cfg<D>::LPG];
 };
 
-// index into the page table of the page holding this wave's keys of tile c
-// (any valid index for the block-key tile, which reads no page)
-template <bool P2>
-__device__ __forceinline__ int page_index(const Cur& c, const Args& a, int wq) {
-    if (!is_prefix(c, a)) return 0;
-    const int j0 = min(c.t * kTile + 16 * wq, c.L - 1);
-    return c.b * a.max_pages + page_of<P2>(a, j0);
-}
-
 // Issue this wave's loads of tile c. Loads are unconditional and their
 // registers are not touched until they are stored to LDS: a key past the end of
 // a partial tile reads the tile's last valid key instead (finite, weight exactly
@@ -256,25 +252,27 @@ __device__ __forceinline__ void load_tile(Regs<D>& r, const Cur& c, int page, co
     for (int i = 0; i < C::LPG; ++i) r.x[i] = ldg_nt(base + off[i]);
 }
 
-// registers -> LDS half tile, chunk c of row r at chunk position c ^ swz(r)
+// registers -> LDS half tile with row pitch `pitch`
 template <int D>
-__device__ __forceinline__ void store_tile(const Regs<D>& r, uint8_t* buf, int wq, int lane) {
+__device__ __forceinline__ void store_tile(const Regs<D>& r, uint8_t* buf, int pitch, int wq, int lane) {
     using C = Cfg<D>;
-    const int ch = lane % C::CPR;
+    uint8_t* p = buf + (16 * wq + lane / C::CPR) * pitch + 16 * (lane % C::CPR);
 #pragma unroll
-    for (int i = 0; i < C::LPG; ++i) {
-        const int row = 16 * wq + C::RPI * i + lane / C::CPR;
-        *reinterpret_cast<u32x4*>(buf + row * C::ROWB + 16 * (ch ^ swz<D>(row))) = r.x[i];
-    }
+    for (int i = 0; i < C::LPG; ++i) *reinterpret_cast<u32x4*>(p + C::RPI * i * pitch) = r.x[i];
 }
 
 // Workgroup barrier ordering LDS accesses only: waits for this wave's own LDS
 // writes, not for the global loads in flight (a plain __syncthreads() would
 // wait for those too and drain the prefetch).
+// The scheduling barriers keep every instruction on its side of the
+// s_barrier: register-only work (MFMAs) would otherwise drift across it and
+// into the next interval.
 __device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 __device__ __forceinline__ bf16x8 lds16(const uint8_t* p) {
@@ -316,7 +314,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
                                                                 const int* __restrict__ ctx_len) {
     using C = Cfg<D>;
     // K tiles (two buffers), then V tiles (two buffers)
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * C::TILEB];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * C::KTILE + 2 * C::VTILE];
     __shared__ int sh[kThreads + 4];
 
     const int tid = threadIdx.x;
@@ -352,37 +350,71 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
     // ---- this group's half of every tile ----
     const uint16_t* src_c = grp ? a.Vc : a.Kc;
     const uint16_t* src_d = grp ? a.Vd : a.Kd;
-    uint8_t* const mybuf = smem + grp * 2 * C::TILEB;
     const uint8_t* const Kbuf = smem;
-    const uint8_t* const Vbuf = smem + 2 * C::TILEB;
+    const uint8_t* const Vbuf = smem + 2 * C::KTILE;
+    uint8_t* const mybuf = smem + (grp ? 2 * C::KTILE : 0);
+    const int mypitch = grp ? C::VROW : C::KROW;
+    const int mytile = grp ? C::VTILE : C::KTILE;
     // page ids through a bounds-checked buffer resource (an empty table reads 0)
     const __amdgpu_buffer_rsrc_t ptab = __builtin_amdgcn_make_buffer_rsrc(
         (void*)page_table, (short)0, page_table ? a.B * a.max_pages * 4 : 0, 0x00020000);
 
-    // Load pipeline: tile j's registers are filled two feeds before they are
-    // stored, and its page id one feed before that. Every feed issues the same
-    // loads (past the segment's end it reloads the last tile), so the wait
-    // counts the compiler derives are exact and never drain the pipeline.
-    Regs<D> R[2];
+    // Page ids come in batches of 64 tiles: lane l walks the tile stream from
+    // the load cursor to tile first + l (across pair and sequence boundaries)
+    // and fetches the page of its 16 keys with one buffer load for the batch.
+    // Per tile the id is then a readlane, so the K/V loads never wait on a
+    // page-table read that sits behind other loads in the (in-order) counter.
+    auto page_batch = [&](const Cur& c, int first) __attribute__((always_inline)) {
+        int idx = 0;
+        if (lane < n - first) {  // tiles past the segment stay at index 0
+            int b = c.b, pl = c.pl, t = c.t + lane, L = c.L, units = c.units;
+            while (t >= units) {
+                t -= units;
+                if (++pl == mult) {
+                    pl = 0;
+                    do {
+                        ++b;
+                        L = seq_len(a, ctx_len, b);
+                        units = (L + kTile - 1) / kTile + a.has_den;
+                    } while (units == 0);
+                }
+            }
+            if (t < units - a.has_den) idx = b * a.max_pages + page_of<P2>(a, min(t * kTile + 16 * wq, L - 1));
+        }
+        return __builtin_amdgcn_raw_buffer_load_b32(ptab, idx * 4, 0, 0);
+    };
+
+    // Load pipeline: tile j's registers are filled kNR tiles before they are
+    // stored. Every issue loads a whole tile (past the segment's end it reloads
+    // the last one), so the wait counts the compiler derives are exact and
+    // never drain the pipeline.
+    Regs<D> R[kNR];
     Cur cl = cc;  // next tile to load
     int ul = 0;   // its index in the segment
-    int pg_cur = __builtin_amdgcn_raw_buffer_load_b32(ptab, page_index<P2>(cl, a, wq) * 4, 0, 0);
+    int pg_base = 0;
+    int pgl = page_batch(cl, 0);
     auto issue = [&](Regs<D>& r) __attribute__((always_inline)) {
-        Cur nx = cl;
-        if (ul + 1 < n) advance(nx, a, ctx_len);
-        const int pg_next = __builtin_amdgcn_raw_buffer_load_b32(ptab, page_index<P2>(nx, a, wq) * 4, 0, 0);
-        load_tile<D, P2>(r, cl, __builtin_amdgcn_readfirstlane(pg_cur), src_c, src_d, a, wq, lane);
-        pg_cur = pg_next;
-        cl = nx;
-        if (ul + 1 < n) ++ul;
+        if (ul - pg_base == 64) {
+            pgl = page_batch(cl, ul);
+            pg_base = ul;
+        }
+        load_tile<D, P2>(r, cl, __builtin_amdgcn_readlane(pgl, ul - pg_base), src_c, src_d, a, wq, lane);
+        if (ul + 1 < n) {
+            advance(cl, a, ctx_len);
+            ++ul;
+        }
     };
-    issue(R[0]);
-    issue(R[1]);
-    // store tile j (if it exists) from R[j % 2] and refill that set with tile j + 2
+#pragma unroll
+    for (int k = 0; k < kNR; ++k) issue(R[k]);
+    // Tile j's registers are R[j % kNR]: stored to LDS buffer j % 2, then
+    // refilled with tile j + kNR.
+    auto store = [&](auto J_, int j) __attribute__((always_inline)) {
+        constexpr int J = decltype(J_)::value;  // j % 2
+        if (j < n) store_tile<D>(R[J % kNR], mybuf + J * mytile, mypitch, wq, lane);
+    };
     auto feed = [&](auto J_, int j) __attribute__((always_inline)) {
-        constexpr int J = decltype(J_)::value;
-        if (j < n) store_tile<D>(R[J], mybuf + J * C::TILEB, wq, lane);
-        issue(R[J]);
+        store(J_, j);
+        issue(R[decltype(J_)::value % kNR]);
     };
 
     // ---- per-wave state ----
@@ -392,17 +424,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
     bf16x8 pf[4];
     float m2 = -INFINITY, lsum = 0.f;
     int piece_t0 = 0;
-    // Lane-constant parts of the swizzled LDS addresses. Chunk (2*ds + hl) of
-    // row l32 sits at 16 * ((2*ds + hl) ^ swz(l32)) = 16 * (hl ^ swz(l32)) ^ 32*ds
-    // within the 256-byte-aligned row, so every score read is one per-lane
-    // offset XOR a per-step constant. Likewise the V reads: chunk 4*dt + vchunk
-    // of row vrow sits at 16 * (vchunk ^ swz(vrow)) ^ 64*dt.
-    const int vrow = 4 * hl + ((lane & 15) >> 2);
-    const int vchunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-    const int vbyte = 8 * (lane & 1);
-    const int kaddr = l32 * C::ROWB + 16 * (hl ^ swz<D>(l32));
-    const int vaddr0 = vrow * C::ROWB + 16 * (vchunk ^ swz<D>(vrow)) + vbyte;
-    const int vaddr1 = (vrow + 8) * C::ROWB + 16 * (vchunk ^ swz<D>(vrow + 8)) + vbyte;
+    // lane parts of the LDS operand addresses: score reads take chunk
+    // 2*ds + hl of row l32 (+32 mt); V reads take bytes vbyte.. of chunk
+    // 4*dt + vchunk of row vrow (+16 ks, +8 for the second half)
+    const int kaddr = l32 * C::KROW + 16 * hl;
+    const int vaddr = (4 * hl + ((lane & 15) >> 2)) * C::VROW + 16 * (2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) +
+                      8 * (lane & 1);
 
     // query rows of the pair at c (a row past S*G reads the last row; it is never written)
     auto load_q = [&](const Cur& c) __attribute__((always_inline)) {
@@ -415,12 +442,54 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
     };
 
     // matrix phase: S^T of the tile in K buffer KB (if QK), then O^T += V^T P^T
-    // for the previous tile, in V buffer VB (if PV); the two chains interleave
+    // for the previous tile, in V buffer VB (if PV). The operands of 16-key
+    // step ks+1 are read from LDS while the MFMAs of step ks run.
+    struct Frag {
+        bf16x8 k[C::DS / 4][2];
+        bf16x8 v[C::DT];
+    };
     auto matrix = [&](auto QK_, auto PV_, auto KB_, auto VB_) __attribute__((always_inline)) {
         constexpr bool QK = decltype(QK_)::value;
         constexpr bool PV = decltype(PV_)::value;
-        const uint8_t* Kst = Kbuf + decltype(KB_)::value * C::TILEB;
-        const uint8_t* Vst = Vbuf + decltype(VB_)::value * C::TILEB;
+        const uint8_t* Kst = Kbuf + decltype(KB_)::value * C::KTILE + kaddr;
+        const uint8_t* Vst = Vbuf + decltype(VB_)::value * C::VTILE + vaddr;
+        auto read = [&](Frag& f, auto KS_) __attribute__((always_inline)) {
+            constexpr int ks = decltype(KS_)::value;
+            if constexpr (QK) {
+#pragma unroll
+                for (int dd = 0; dd < C::DS / 4; ++dd)
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt)
+                        f.k[dd][mt] = lds16(Kst + mt * 32 * C::KROW + 32 * (ks * (C::DS / 4) + dd));
+            }
+            if constexpr (PV) {
+                // V sits in LDS as [key][d]; the transposing read hands lane l the four keys
+                // kb..kb+3 of column d = 32*dt + l%32, with kb = 16*ks + 8*half + 4*(l/32):
+                // exactly the keys its P^T slots hold.
+#pragma unroll
+                for (int dt = 0; dt < C::DT; ++dt) {
+                    const uint8_t* p0 = Vst + ks * 16 * C::VROW + 64 * dt;
+                    const i16x4 pair[2] = {lds_tr(p0), lds_tr(p0 + 8 * C::VROW)};
+                    f.v[dt] = __builtin_bit_cast(bf16x8, pair);
+                }
+            }
+        };
+        auto mma = [&](const Frag& f, auto KS_) __attribute__((always_inline)) {
+            constexpr int ks = decltype(KS_)::value;
+            if constexpr (QK) {
+#pragma unroll
+                for (int dd = 0; dd < C::DS / 4; ++dd)
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt)
+                        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.k[dd][mt], qf[ks * (C::DS / 4) + dd],
+                                                                          sacc[mt], 0, 0, 0);
+            }
+            if constexpr (PV) {
+#pragma unroll
+                for (int dt = 0; dt < C::DT; ++dt)
+                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.v[dt], pf[ks], oacc[dt], 0, 0, 0);
+            }
+        };
         __builtin_amdgcn_s_setprio(1);
         if constexpr (QK) {
 #pragma unroll
@@ -428,39 +497,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
 #pragma unroll
                 for (int e = 0; e < 16; ++e) sacc[mt][e] = 0.f;
         }
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            if constexpr (QK) {
-#pragma unroll
-                for (int dd = 0; dd < C::DS / 4; ++dd) {
-                    const int ds = ks * (C::DS / 4) + dd;
-                    bf16x8 kf[2];
-#pragma unroll
-                    for (int mt = 0; mt < 2; ++mt)
-                        kf[mt] = lds16(Kst + (kaddr ^ (32 * ds)) + mt * 32 * C::ROWB);
-#pragma unroll
-                    for (int mt = 0; mt < 2; ++mt)
-                        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[mt], qf[ds], sacc[mt], 0, 0, 0);
-                }
-            }
-            if constexpr (PV) {
-                // V sits in LDS as [key][d]; the transposing read hands lane l the four keys
-                // kb..kb+3 of column d = 32*dt + l%32, with kb = 16*ks + 8*half + 4*(l/32):
-                // exactly the keys its P^T slots hold.
-                bf16x8 vf[C::DT];
-#pragma unroll
-                for (int dt = 0; dt < C::DT; ++dt) {
-                    const uint8_t* p0 = Vst + (vaddr0 ^ (64 * dt)) + ks * 16 * C::ROWB;
-                    const uint8_t* p1 = Vst + (vaddr1 ^ (64 * dt)) + ks * 16 * C::ROWB;
-                    const i16x4 pair[2] = {lds_tr(p0), lds_tr(p1)};
-                    vf[dt] = __builtin_bit_cast(bf16x8, pair);
-                }
-#pragma unroll
-                for (int dt = 0; dt < C::DT; ++dt)
-                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dt], pf[ks], oacc[dt], 0, 0, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, 2>;
+        using I3 = std::integral_constant<int, 3>;
+        Frag f0, f1;
+        read(f0, I0{});
+        read(f1, I1{});
+        mma(f0, I0{});
+        __builtin_amdgcn_sched_barrier(0);
+        read(f0, I2{});
+        mma(f1, I1{});
+        __builtin_amdgcn_sched_barrier(0);
+        read(f1, I3{});
+        mma(f0, I2{});
+        __builtin_amdgcn_sched_barrier(0);
+        mma(f1, I3{});
     };
 
     // A finished piece of pair pl of sequence b: the normalised output if the
@@ -522,6 +574,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
     auto vector = [&](auto P_, int i) __attribute__((always_inline)) {
         constexpr int P = decltype(P_)::value;  // i % 2
         __builtin_amdgcn_s_setprio(0);
+        // my half of tile i+1 into LDS first: the writes complete while the
+        // softmax runs (its buffer was last read two intervals ago)
+        store(std::integral_constant<int, 1 - P>{}, i + 1);
         const bool close_prev = i > 0 && prev_ends;
         if (close_prev) epilogue(prev_b, prev_pl, prev_g, piece_t0 == 0);
         if (i == 0 || close_prev) {
@@ -573,7 +628,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
         }
         lsum += ls;
         // next tile: its query rows if it starts a new piece (issued before the
-        // staging loads, so waiting for them leaves those in flight), then staging
+        // staging loads, so waiting for them leaves those in flight), then the
+        // loads of tile i+1+kNR
         prev_ends = cc.t == cc.units - 1;
         prev_b = cc.b;
         prev_pl = cc.pl;
@@ -582,7 +638,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
             advance(cc, a, ctx_len);
             if (cc.t == 0) load_q(cc);
         }
-        feed(std::integral_constant<int, 1 - P>{}, i + 1);
+        issue(R[(1 - P) % kNR]);
     };
 
     // ---- prologue: group 0 stages K of tile 0 before the first barrier, group 1
