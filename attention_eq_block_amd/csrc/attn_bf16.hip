@@ -207,10 +207,6 @@ __device__ __forceinline__ int slot_of(const Args& a, int j) {
     return P2 ? (j & (a.page_size - 1)) : j % a.page_size;
 }
 
-__device__ __forceinline__ u32x4 ldg_nt(const uint16_t* p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-}
-
 // ---- tile staging: global -> registers -> LDS ------------------------------
 // Wave w (0..3 within its group) moves keys 16w .. 16w+15 of its group's half
 // tile: load instruction i covers rows 16w + RPI*i + lane/CPR, 16-byte chunk
@@ -221,35 +217,45 @@ struct Regs {
     u32x4 x[Cfg<D>::LPG];
 };
 
-// Issue this wave's loads of tile c. Loads are unconditional and their
-// registers are not touched until they are stored to LDS: a key past the end of
-// a partial tile reads the tile's last valid key instead (finite, weight exactly
-// 0); a page id outside [0, num_pages) is clamped, so a corrupt table reads
-// wrong data but never faults.
+// Issue this wave's loads of tile c: keys 16*wq .. 16*wq+15 of the tile, load
+// instruction i covering rows RPI*i + lane/CPR of them (16-byte chunk
+// lane%CPR). The 16 keys lie in one page (page_size is a multiple of 16), so a
+// block of the prefix is a uniform base plus the lane's fixed offset `loff`.
+// Only a block that reaches past the prefix end clamps its rows to the last key
+// (finite data, weight exactly 0); a block wholly past the end reads the block
+// holding the last key. A page id outside [0, num_pages) is clamped, so a
+// corrupt table reads wrong data but never faults. Loads are unconditional and
+// their registers are not touched until they are stored to LDS.
 template <int D, bool P2>
 __device__ __forceinline__ void load_tile(Regs<D>& r, const Cur& c, int page, const uint16_t* src_c,
-                                          const uint16_t* src_d, const Args& a, int wq, int lane) {
+                                          const uint16_t* src_d, const Args& a, int wq, int lane, unsigned loff) {
     using C = Cfg<D>;
-    const int ch = lane % C::CPR;
-    const int lrow = lane / C::CPR;
-    const uint16_t* base;
+    const int ch = lane % C::CPR, lrow = lane / C::CPR;
+    const char* base;
     unsigned off[C::LPG];
     if (is_prefix(c, a)) {
+        int j0 = c.t * kTile + 16 * wq;
+        if (j0 >= c.L) j0 = (c.L - 1) & ~15;
+        const int last = c.L - 1 - j0;  // rows 0..last of the block are keys
         page = min(max(page, 0), a.num_pages - 1);
-        base = src_c + ((long long)page * a.Hkv + c.g) * a.page_size * D;
+        base = reinterpret_cast<const char*>(src_c + (((long long)page * a.Hkv + c.g) * a.page_size +
+                                                      slot_of<P2>(a, j0)) * D);
+        if (last >= 15) {
 #pragma unroll
-        for (int i = 0; i < C::LPG; ++i) {
-            const int j = min(c.t * kTile + 16 * wq + C::RPI * i + lrow, c.L - 1);
-            off[i] = (unsigned)(slot_of<P2>(a, j) * D + ch * 8);
+            for (int i = 0; i < C::LPG; ++i) off[i] = loff + (unsigned)(C::RPI * i * D * 2);
+        } else {
+#pragma unroll
+            for (int i = 0; i < C::LPG; ++i) off[i] = (unsigned)((min(C::RPI * i + lrow, last) * D + ch * 8) * 2);
         }
     } else {
-        base = src_d + (long long)c.b * a.dsb + (long long)c.g * a.dsh;
+        base = reinterpret_cast<const char*>(src_d + (long long)c.b * a.dsb + (long long)c.g * a.dsh);
 #pragma unroll
         for (int i = 0; i < C::LPG; ++i)
-            off[i] = (unsigned)(min(16 * wq + C::RPI * i + lrow, a.S - 1) * a.dss + ch * 8);
+            off[i] = (unsigned)((min(16 * wq + C::RPI * i + lrow, a.S - 1) * a.dss + ch * 8) * 2);
     }
 #pragma unroll
-    for (int i = 0; i < C::LPG; ++i) r.x[i] = ldg_nt(base + off[i]);
+    for (int i = 0; i < C::LPG; ++i)
+        r.x[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + off[i]));
 }
 
 // registers -> LDS half tile with row pitch `pitch`
@@ -389,6 +395,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
     // the last one), so the wait counts the compiler derives are exact and
     // never drain the pipeline.
     Regs<D> R[kNR];
+    const unsigned loff = (unsigned)(((lane / C::CPR) * D + (lane % C::CPR) * 8) * 2);  // byte offset in a block
     Cur cl = cc;  // next tile to load
     int ul = 0;   // its index in the segment
     int pg_base = 0;
@@ -398,7 +405,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
             pgl = page_batch(cl, ul);
             pg_base = ul;
         }
-        load_tile<D, P2>(r, cl, __builtin_amdgcn_readlane(pgl, ul - pg_base), src_c, src_d, a, wq, lane);
+        load_tile<D, P2>(r, cl, __builtin_amdgcn_readlane(pgl, ul - pg_base), src_c, src_d, a, wq, lane, loff);
         if (ul + 1 < n) {
             advance(cl, a, ctx_len);
             ++ul;
