@@ -18,10 +18,18 @@ attention layer (B*S*layers*steps / time), the attention call's roofline, and
 the CPU oracle on a bounded sample as a baseline.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload loop|single|ragged|long]
+    python bench.py --copy-calibration   # a plain device copy of known size, for counter scaling
+
+roofline.traffic is the HBM traffic of one attention call measured with
+rocprofv3 FETCH_SIZE / WRITE_SIZE counters, scaled by the ratio the same
+counters give for the plain copy; it is read from profiles/attn_loop_hbm_traffic.txt
+and reported only while the kernel source still hashes to the value recorded
+there (otherwise null).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -36,6 +44,31 @@ sys.path.insert(0, ROOT)
 from attention_eq_block_amd import api, synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_loop_hbm_traffic.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "attention_eq_block_amd", "csrc", "attn_bf16.hip")
+COPY_BYTES = 1 << 30
+
+
+def kernel_source_hash():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per attention call from the committed counter summary, or None when
+    the summary is missing or was taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
 METRIC = "noisy-block tokens/s per attn layer (S=16); achieved HBM TB/s vs peak"
 
 
@@ -187,7 +220,7 @@ def run_loop(args):
                    "denoise_steps_per_block": steps_per_block, "blocks_per_s": B * args.steps / wall,
                    "attn_call_us": call_ms * 1e3, "attn_call_tokens_per_s": B * S / (call_ms * 1e-3)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": "tt_block_attn (attn_bf16_kernel + attn_bf16_finalize), one layer",
                      "algorithmic_bytes": algo},
     }
@@ -228,6 +261,17 @@ def run_single(args, name):
     return res
 
 
+def copy_calibration():
+    """A plain device-to-device copy of COPY_BYTES, five times: the counter reference
+    for FETCH_SIZE / WRITE_SIZE (each launch reads and writes COPY_BYTES)."""
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.int32, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 5}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -237,6 +281,7 @@ def main():
     ap.add_argument("--gamma", type=float, default=0.8)
     ap.add_argument("--temperature", type=float, default=0.1)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true", help="run only the counter-reference copy")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (the data-parallel "
@@ -246,6 +291,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     res = run_loop(args) if args.workload == "loop" else run_single(args, args.workload)
     print(json.dumps(res))
 
