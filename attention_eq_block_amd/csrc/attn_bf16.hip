@@ -104,6 +104,7 @@ struct Args {
     float* LSE;
     float* part_o;
     float* part_lse;
+    int* units_before;  // [0]: total units W; [1 + b]: units of the sequences before b
     int B, S, Hq, Hkv, G, n_rb, has_den, n_seg;
     float c_log2;  // softmax_scale * log2(e)
 };
@@ -116,22 +117,19 @@ __device__ __forceinline__ int seq_len(const Args& a, const int* __restrict__ ct
 }
 __device__ __forceinline__ int units_for(const Args& a, int L) { return (L + kTile - 1) / kTile + a.has_den; }
 
-// Block-wide: total units W and, for unit u (u >= 0), the sequence holding it
-// and the first unit of that sequence. For b_prefix >= 0 instead, also the
-// first unit of sequence b_prefix. `sh` is LDS scratch of NTHR + 4 ints.
+// Block-wide, one pass over ctx_len: total units W and, for segment `seg` of
+// n_seg equal segments, its first unit u0, the sequence b0 holding it and the
+// first unit c0 of that sequence; with `before` set, also W and every
+// sequence's first unit there. `sh` is LDS scratch of NTHR + 4 ints.
 template <int NTHR>
-__device__ void scan_units(const Args& a, const int* __restrict__ ctx_len, int u, int b_prefix, int* sh, int& W,
-                           int& b_out, int& c_out) {
+__device__ void scan_segment(const Args& a, const int* __restrict__ ctx_len, int seg, int* sh, int& W, int& u0,
+                             int& b0, int& c0, int* before) {
     const int t = threadIdx.x;
     const int mult = a.Hkv * a.n_rb;
     const int chunk = (a.B + NTHR - 1) / NTHR;
     const int lo = min(a.B, t * chunk), hi = min(a.B, lo + chunk);
-    int sum = 0, before = 0;
-    for (int b = lo; b < hi; ++b) {
-        const int n = units_for(a, ctx_len ? clamp_len(ctx_len[b], a.Lmax) : 0) * mult;
-        sum += n;
-        if (b < b_prefix) before += n;
-    }
+    int sum = 0;
+    for (int b = lo; b < hi; ++b) sum += units_for(a, ctx_len ? clamp_len(ctx_len[b], a.Lmax) : 0) * mult;
     sh[t] = sum;
     __syncthreads();
     for (int off = 1; off < NTHR; off <<= 1) {
@@ -143,22 +141,30 @@ __device__ void scan_units(const Args& a, const int* __restrict__ ctx_len, int u
     const int incl = sh[t];
     const int excl = incl - sum;
     W = sh[NTHR - 1];
+    if (before) {
+        if (t == 0) before[0] = W;
+        int c = excl;
+        for (int b = lo; b < hi; ++b) {
+            before[1 + b] = c;
+            c += units_for(a, ctx_len ? clamp_len(ctx_len[b], a.Lmax) : 0) * mult;
+        }
+    }
+    const int seg_len = (W + a.n_seg - 1) / a.n_seg;
+    u0 = seg * seg_len;
     __syncthreads();
-    if (t == 0) { sh[NTHR] = 0; sh[NTHR + 1] = 0; sh[NTHR + 2] = 0; }
+    if (t == 0) { sh[NTHR] = 0; sh[NTHR + 1] = 0; }
     __syncthreads();
-    if (u >= 0 && u >= excl && u < incl) {
+    if (u0 >= excl && u0 < incl) {
         int c = excl;
         for (int b = lo; b < hi; ++b) {
             const int n = units_for(a, ctx_len ? clamp_len(ctx_len[b], a.Lmax) : 0) * mult;
-            if (u < c + n) { sh[NTHR] = b; sh[NTHR + 1] = c; break; }
+            if (u0 < c + n) { sh[NTHR] = b; sh[NTHR + 1] = c; break; }
             c += n;
         }
     }
-    if (b_prefix >= 0 && b_prefix >= lo && b_prefix < hi) sh[NTHR + 2] = excl + before;
-    else if (b_prefix >= 0 && b_prefix == a.B && t == NTHR - 1) sh[NTHR + 2] = incl;
     __syncthreads();
-    if (u >= 0) { b_out = sh[NTHR]; c_out = sh[NTHR + 1]; }
-    if (b_prefix >= 0) c_out = sh[NTHR + 2];
+    b0 = sh[NTHR];
+    c0 = sh[NTHR + 1];
     __syncthreads();
 }
 
@@ -333,14 +339,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
     const int per_xcd = a.n_seg / 8;
     const int seg = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
 
-    int W, b0, c0;
-    scan_units<kThreads>(a, ctx_len, -1, -1, sh, W, b0, c0);  // total units W
+    int W, u0, b0, c0;
+    scan_segment<kThreads>(a, ctx_len, seg, sh, W, u0, b0, c0, seg == 0 ? a.units_before : nullptr);
     W = __builtin_amdgcn_readfirstlane(W);
+    u0 = __builtin_amdgcn_readfirstlane(u0);
     const int seg_len = (W + a.n_seg - 1) / a.n_seg;
-    const int u0 = seg * seg_len;
     const int n = min(W, u0 + seg_len) - u0;  // tiles of this segment
     if (n <= 0) return;
-    scan_units<kThreads>(a, ctx_len, u0, -1, sh, W, b0, c0);
     b0 = __builtin_amdgcn_readfirstlane(b0);
     c0 = __builtin_amdgcn_readfirstlane(c0);
 
@@ -693,22 +698,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
 }
 
 // Merge the per-segment partials of every pair that segment boundaries cut,
-// and write O = 0, LSE = -inf for pairs with no keys at all.
-// Grid: n_pairs * 16 workgroups of 256 threads, 16 rows each.
+// and write O = 0, LSE = -inf for pairs with no keys at all. The pair's
+// segments follow from the unit counts the main kernel left in the workspace.
+// Grid: n_pairs * 16 workgroups of 256 threads, 16 rows each; a row's 16
+// threads take D/16 consecutive floats each, and every partial a thread reads
+// is an independent load.
 template <int D>
 __global__ __launch_bounds__(kFinThreads) void attn_bf16_finalize(Args a, const int* __restrict__ ctx_len) {
-    __shared__ int sh[kFinThreads + 4];
     const int mult = a.Hkv * a.n_rb;
     const int p = blockIdx.x / 16, chunk = blockIdx.x % 16;
     const int b = p / mult, pl = p % mult;
     const int g = pl / a.n_rb, rb = pl % a.n_rb;
-    int W, bdummy, Cb;
-    scan_units<kFinThreads>(a, ctx_len, -1, b, sh, W, bdummy, Cb);
+    const int W = a.units_before[0];
     const int units = units_for(a, ctx_len ? clamp_len(ctx_len[b], a.Lmax) : 0);  // tiles per pair
     const int seg_len = (W + a.n_seg - 1) / a.n_seg;
     int s0 = 0, s1 = -1;
     if (units > 0) {
-        const int U = Cb + pl * units;
+        const int U = a.units_before[1 + b] + pl * units;
         s0 = U / seg_len;
         s1 = (U + units - 1) / seg_len;
         if (s0 == s1) return;  // written by the main kernel
@@ -719,23 +725,38 @@ __global__ __launch_bounds__(kFinThreads) void attn_bf16_finalize(Args a, const 
     if (rr >= a.S * a.G) return;
     const int s = rr / a.G, h = g * a.G + rr % a.G;
     const long long ob = (long long)b * a.osb + (long long)s * a.oss + (long long)h * a.osh;
+    // partials in groups of four, each group's loads issued together (an index
+    // past s1 rereads slot s1 and gets weight 0)
     float M = -INFINITY;
-    for (int sg = s0; sg <= s1; ++sg) M = fmaxf(M, a.part_lse[(long long)(sg + p) * kRows + rl]);
+    for (int sg0 = s0; sg0 <= s1; sg0 += 4) {
+        float l[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) l[j] = a.part_lse[(long long)(min(sg0 + j, s1) + p) * kRows + rl];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) M = fmaxf(M, l[j]);
+    }
     constexpr int PER = D / 64;  // 4-float chunks per thread
     f32x4 acc[PER];
     for (int k = 0; k < PER; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     float Wsum = 0.f;
     if (M != -INFINITY) {
-        for (int sg = s0; sg <= s1; ++sg) {
-            const long long slot = sg + p;
-            const float l = a.part_lse[slot * kRows + rl];
-            if (l == -INFINITY) continue;
-            const float w = __expf(l - M);
-            Wsum += w;
-            const float* po = a.part_o + (slot * kRows + rl) * D;
-            for (int k = 0; k < PER; ++k) {
-                const f32x4 v = *reinterpret_cast<const f32x4*>(po + ((tid % 16) + 16 * k) * 4);
-                acc[k] += w * v;
+        for (int sg0 = s0; sg0 <= s1; sg0 += 4) {
+            float l[4];
+            f32x4 v[4][PER];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const long long slot = min(sg0 + j, s1) + p;
+                l[j] = a.part_lse[slot * kRows + rl];
+                const float* po = a.part_o + (slot * kRows + rl) * D;
+#pragma unroll
+                for (int k = 0; k < PER; ++k) v[j][k] = *reinterpret_cast<const f32x4*>(po + ((tid % 16) + 16 * k) * 4);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float w = (sg0 + j <= s1 && l[j] != -INFINITY) ? __expf(l[j] - M) : 0.f;
+                Wsum += w;
+#pragma unroll
+                for (int k = 0; k < PER; ++k) acc[k] += w * v[j][k];
             }
         }
     }
@@ -772,7 +793,8 @@ AttnPlan plan_attn_bf16(const tt_block_attn_params& p, int n_cu) {
     pl.n_slots = pl.n_seg + pl.n_pairs;
     pl.ws_part_o = (size_t)pl.n_slots * kRows * p.head_dim * sizeof(float);
     pl.ws_part_lse = (size_t)pl.n_slots * kRows * sizeof(float);
-    pl.ws_total = pl.ws_part_o + pl.ws_part_lse + 256;
+    pl.ws_units = ((size_t)(p.B + 1) * sizeof(int) + 255) / 256 * 256;
+    pl.ws_total = pl.ws_part_o + pl.ws_part_lse + pl.ws_units + 256;
     return pl;
 }
 
@@ -797,6 +819,7 @@ tt_status launch_attn_bf16(const tt_block_attn_params& p, const AttnPlan& pl, vo
     char* w = static_cast<char*>(ws);
     a.part_o = reinterpret_cast<float*>(w);
     a.part_lse = reinterpret_cast<float*>(w + pl.ws_part_o);
+    a.units_before = reinterpret_cast<int*>(w + pl.ws_part_o + pl.ws_part_lse);
     a.B = p.B; a.S = p.S; a.Hq = p.Hq; a.Hkv = p.Hkv; a.G = p.Hq / p.Hkv;
     a.n_rb = pl.n_rb;
     a.has_den = p.Kden ? 1 : 0;

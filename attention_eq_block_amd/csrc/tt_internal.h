@@ -27,6 +27,7 @@ struct AttnPlan {
     int n_slots;   // partial slots: n_seg + n_pairs
     size_t ws_part_o;    // bytes of partial O
     size_t ws_part_lse;  // bytes of partial LSE
+    size_t ws_units;     // bytes of the per-sequence unit offsets the merge reads
     size_t ws_total;
 };
 

@@ -92,6 +92,36 @@ def test_empty_key_set():
     assert torch.all(O.float() == 0) and torch.all(torch.isneginf(L))
 
 
+def test_empty_sequences_among_others():
+    """Sequences with no keys at all next to ones with a prefix (no block keys): the empty ones get
+    O = 0, LSE = -inf, the others their attention; pairs of the long ones span many segments."""
+    c = case(5, 16, 32, 2, 128, [0, 300, 0, 4000, 0], with_den=False, shuffle_pages=True)
+    print(run_full(c, what="empty sequences among prefix-only ones"))
+
+
+def test_workspace_reused_across_calls_and_garbage():
+    """One workspace, filled with random bytes, serves consecutive calls whose segment cuts differ:
+    the per-pair arrival counts need no clearing between calls."""
+    cases = [case(4, 16, 32, 2, 128, [4096, 900, 3000, 17]), case(4, 16, 32, 2, 128, [64, 5000, 128, 2500]),
+             case(4, 16, 32, 2, 128, [4096, 900, 3000, 17])]
+    inps = [synth.make_attn_inputs(c, seed=i) for i, c in enumerate(cases)]
+    nb = 0
+    for inp in inps:
+        p = api.attn_params(*[to_dev(inp)[k] for k in ("Q", "Kc", "Vc", "page_table", "ctx_len", "Kd", "Vd")],
+                            page_size=inp["page_size"], max_ctx_len=int(inp["ctx_len"].max()), scale=inp["scale"])
+        nb = max(nb, api.block_attn_workspace_bytes(p))
+    g = torch.Generator(device="cuda").manual_seed(7)
+    ws = torch.randint(0, 256, (nb,), dtype=torch.uint8, device="cuda", generator=g)
+    for i, (c, inp) in enumerate(zip(cases, inps)):
+        d = to_dev(inp)
+        O, L = api.block_attn(d["Q"], d["Kc"], d["Vc"], d["page_table"], d["ctx_len"], d["Kd"], d["Vd"],
+                              page_size=inp["page_size"], max_ctx_len=int(inp["ctx_len"].max()), scale=inp["scale"],
+                              workspace=ws)
+        torch.cuda.synchronize()
+        Or, Lr = oracle_attn(inp)
+        print(check_attn(O, L, Or, Lr, c.dtype, f"call {i} on a shared workspace"))
+
+
 def test_prefix_only_and_block_only():
     c = case(3, 16, 32, 2, 128, [300, 64, 1000], with_den=False, shuffle_pages=True)
     print(run_full(c, what="prefix only"))
