@@ -274,16 +274,18 @@ __device__ __forceinline__ void store_tile(const Regs<D>& r, uint8_t* buf, int p
 }
 
 // Workgroup barrier ordering LDS accesses only: waits for this wave's own LDS
-// writes, not for the global loads in flight (a plain __syncthreads() would
-// wait for those too and drain the prefetch).
-// The scheduling barriers keep every instruction on its side of the
-// s_barrier: register-only work (MFMAs) would otherwise drift across it and
-// into the next interval.
+// reads and writes (lgkmcnt), not for the global loads in flight. A
+// __syncthreads() or a workgroup fence would also wait for every global load,
+// since direct-to-LDS loads may be pending, and drain the prefetch; the data
+// those loads bring is waited for where it is read (each wave reads only its
+// own). The empty asm statements keep the compiler from moving memory
+// accesses across, the scheduling barriers every other instruction.
 __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -328,6 +330,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
     // K tiles (two buffers), then V tiles (two buffers)
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * C::KTILE + 2 * C::VTILE];
     __shared__ int sh[kThreads + 4];
+    __shared__ int pgs[kWaves][2][64];  // page-id batches of each wave
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -370,15 +373,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
     const __amdgpu_buffer_rsrc_t ptab = __builtin_amdgcn_make_buffer_rsrc(
         (void*)page_table, (short)0, page_table ? a.B * a.max_pages * 4 : 0, 0x00020000);
 
-    // Page ids come in batches of 64 tiles: lane l walks the tile stream from
-    // the load cursor to tile first + l (across pair and sequence boundaries)
-    // and fetches the page of its 16 keys with one buffer load for the batch.
-    // Per tile the id is then a readlane, so the K/V loads never wait on a
-    // page-table read that sits behind other loads in the (in-order) counter.
-    auto page_batch = [&](const Cur& c, int first) __attribute__((always_inline)) {
+    // Page ids come in batches of 64 tiles, double-buffered in LDS: lane l
+    // walks the tile stream from cursor c (tile `first` of the segment) by
+    // ahead + l tiles (across pair and sequence boundaries) and fetches the
+    // page of its 16 keys with one direct-to-LDS buffer load for the batch. A
+    // batch is fetched when the one before it comes into use, 64 tiles ahead
+    // of its own first use, after that tile's id is read: the wait for it is
+    // then never more than the wait for the tile loads issued before it (the
+    // in-order load counter reports a page-table read only together with
+    // every load before it).
+    auto page_batch = [&](const Cur& c, int first, int ahead, int buf) __attribute__((always_inline)) {
         int idx = 0;
-        if (lane < n - first) {  // tiles past the segment stay at index 0
-            int b = c.b, pl = c.pl, t = c.t + lane, L = c.L, units = c.units;
+        if (lane + ahead < n - first) {  // tiles past the segment stay at index 0
+            int b = c.b, pl = c.pl, t = c.t + ahead + lane, L = c.L, units = c.units;
             while (t >= units) {
                 t -= units;
                 if (++pl == mult) {
@@ -392,7 +399,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
             }
             if (t < units - a.has_den) idx = b * a.max_pages + page_of<P2>(a, min(t * kTile + 16 * wq, L - 1));
         }
-        return __builtin_amdgcn_raw_buffer_load_b32(ptab, idx * 4, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ptab, (__attribute__((address_space(3))) void*)&pgs[wave][buf][0], 4,
+                                                 idx * 4, 0, 0, 0);
     };
 
     // Load pipeline: tile j's registers are filled kNR tiles before they are
@@ -404,13 +412,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
     Cur cl = cc;  // next tile to load
     int ul = 0;   // its index in the segment
     int pg_base = 0;
-    int pgl = page_batch(cl, 0);
+    int pbuf = 0;  // batch in use
+    page_batch(cl, 0, 0, 0);
+    page_batch(cl, 0, 64, 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): both batches have landed
     auto issue = [&](Regs<D>& r) __attribute__((always_inline)) {
-        if (ul - pg_base == 64) {
-            pgl = page_batch(cl, ul);
+        const bool next_batch = ul - pg_base == 64;
+        if (next_batch) {
             pg_base = ul;
+            pbuf ^= 1;
         }
-        load_tile<D, P2>(r, cl, __builtin_amdgcn_readlane(pgl, ul - pg_base), src_c, src_d, a, wq, lane, loff);
+        const int page = __builtin_amdgcn_readfirstlane(pgs[wave][pbuf][ul - pg_base]);
+        if (next_batch) page_batch(cl, ul, 64, pbuf ^ 1);  // the batch after next, into the one used up
+        load_tile<D, P2>(r, cl, page, src_c, src_d, a, wq, lane, loff);
         if (ul + 1 < n) {
             advance(cl, a, ctx_len);
             ++ul;
@@ -648,7 +662,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
         prev_g = cc.g;
         if (i + 1 < n) {
             advance(cc, a, ctx_len);
-            if (cc.t == 0) load_q(cc);
+            if (cc.t == 0) {
+                // waited for here, once per piece: left pending, the wait
+                // would sit before every tile's score MFMAs
+                load_q(cc);
+                __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            }
         }
         issue(R[(1 - P) % kNR]);
     };
