@@ -29,11 +29,12 @@
 //
 // Schedule inside a workgroup (ping-pong). Eight waves own 32 query rows each
 // and form two groups of four, so that every SIMD runs one wave of each group.
-// Per tile a wave has a matrix phase (scores of tile i and the PV product of
-// tile i-1: MFMA and LDS reads) and a vector phase (softmax of tile i, the
-// staging of the next tile into LDS and the next global loads). Group 1 runs
-// one barrier interval behind group 0, so in every interval one wave on each
-// SIMD issues MFMAs while the other does vector work. Group 0 stages the K
+// Per tile a wave has a matrix phase (scores of tile i, and the softmax and
+// PV product of tile i-1: MFMAs, LDS reads and the exponentials between them)
+// and a vector phase (mask and row max of tile i, the staging of the next tile
+// into LDS, cursor and address work, the next global loads). Group 1 runs one
+// barrier interval behind group 0, so in every interval one wave on each SIMD
+// issues MFMAs while the other does the vector phase. Group 0 stages the K
 // half of every tile and group 1 the V half; each wave moves 16 keys of a
 // tile, so it needs one page id per tile.
 #include <type_traits>
@@ -412,18 +413,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
     Cur cl = cc;  // next tile to load
     int ul = 0;   // its index in the segment
     int pg_base = 0;
+    // The batch in use is also kept in a register (lane l: tile pg_base + l),
+    // so a tile's id is a readlane and its LDS copy is read once per batch.
     int pbuf = 0;  // batch in use
     page_batch(cl, 0, 0, 0);
     page_batch(cl, 0, 64, 1);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): both batches have landed
+    int pgl = pgs[wave][0][lane];
     auto issue = [&](Regs<D>& r) __attribute__((always_inline)) {
-        const bool next_batch = ul - pg_base == 64;
-        if (next_batch) {
+        if (ul - pg_base == 64) {
             pg_base = ul;
             pbuf ^= 1;
+            pgl = pgs[wave][pbuf][lane];
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): here, not before every tile's readlane
+            page_batch(cl, ul, 64, pbuf ^ 1);    // the batch after next, into the one used up
         }
-        const int page = __builtin_amdgcn_readfirstlane(pgs[wave][pbuf][ul - pg_base]);
-        if (next_batch) page_batch(cl, ul, 64, pbuf ^ 1);  // the batch after next, into the one used up
+        const int page = __builtin_amdgcn_readlane(pgl, ul - pg_base);
         load_tile<D, P2>(r, cl, page, src_c, src_d, a, wq, lane, loff);
         if (ul + 1 < n) {
             advance(cl, a, ctx_len);
@@ -446,7 +451,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
     // ---- per-wave state ----
     bf16x8 qf[C::DS];
     f32x16 oacc[C::DT];
-    f32x16 sacc[2];
+    f32x16 sacc[2][2];  // scores of tile j in sacc[j % 2]
     bf16x8 pf[4];
     float m2 = -INFINITY, lsum = 0.f;
     int piece_t0 = 0;
@@ -467,26 +472,32 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
         for (int ds = 0; ds < C::DS; ++ds) qf[ds] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q + ds * 16));
     };
 
-    // matrix phase: S^T of the tile in K buffer KB (if QK), then O^T += V^T P^T
-    // for the previous tile, in V buffer VB (if PV). The operands of 16-key
-    // step ks+1 are read from LDS while the MFMAs of step ks run.
+    // matrix phase of tile j: S^T of tile j from K buffer KB = j % 2 into
+    // sacc[KB] (if QK); the softmax of tile j-1 (scores sacc[VB], running max
+    // from the vector phase before) and O^T += V^T P^T for it from V buffer
+    // VB = (j-1) % 2 (if PV). Per 16-key step ks: the operands of step ks+1
+    // are read from LDS while the step's MFMAs run, and the softmax of keys
+    // 16ks .. 16ks+15 (P^T fragment pf[ks]) fills the vector ALU meanwhile.
+    // The score product runs K-row half outer (steps 0-1 rows 0-31, steps 2-3
+    // rows 32-63), so the new tile's second half comes alive as the old
+    // tile's first half is used up.
+    constexpr int DPS = C::DS / 2;  // d steps of the score product per step
     struct Frag {
-        bf16x8 k[C::DS / 4][2];
+        bf16x8 k[DPS];
         bf16x8 v[C::DT];
     };
     auto matrix = [&](auto QK_, auto PV_, auto KB_, auto VB_) __attribute__((always_inline)) {
         constexpr bool QK = decltype(QK_)::value;
         constexpr bool PV = decltype(PV_)::value;
-        const uint8_t* Kst = Kbuf + decltype(KB_)::value * C::KTILE + kaddr;
-        const uint8_t* Vst = Vbuf + decltype(VB_)::value * C::VTILE + vaddr;
+        constexpr int KB = decltype(KB_)::value, VB = decltype(VB_)::value;
+        const uint8_t* Kst = Kbuf + KB * C::KTILE + kaddr;
+        const uint8_t* Vst = Vbuf + VB * C::VTILE + vaddr;
         auto read = [&](Frag& f, auto KS_) __attribute__((always_inline)) {
             constexpr int ks = decltype(KS_)::value;
             if constexpr (QK) {
 #pragma unroll
-                for (int dd = 0; dd < C::DS / 4; ++dd)
-#pragma unroll
-                    for (int mt = 0; mt < 2; ++mt)
-                        f.k[dd][mt] = lds16(Kst + mt * 32 * C::KROW + 32 * (ks * (C::DS / 4) + dd));
+                for (int dd = 0; dd < DPS; ++dd)
+                    f.k[dd] = lds16(Kst + (ks / 2) * 32 * C::KROW + 32 * ((ks % 2) * DPS + dd));
             }
             if constexpr (PV) {
                 // V sits in LDS as [key][d]; the transposing read hands lane l the four keys
@@ -500,15 +511,26 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
                 }
             }
         };
-        auto mma = [&](const Frag& f, auto KS_) __attribute__((always_inline)) {
+        const float neg = -m2;
+        float ls = 0.f;
+        auto step = [&](const Frag& f, auto KS_) __attribute__((always_inline)) {
             constexpr int ks = decltype(KS_)::value;
+            if constexpr (PV) {
+                f32x8 pv;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[VB][ks >> 1][(ks & 1) * 8 + e], a.c_log2, neg));
+                    ls += pv[e];
+                }
+                pf[ks] = __builtin_convertvector(pv, bf16x8);
+            }
             if constexpr (QK) {
+                constexpr int mt = ks / 2;
 #pragma unroll
-                for (int dd = 0; dd < C::DS / 4; ++dd)
-#pragma unroll
-                    for (int mt = 0; mt < 2; ++mt)
-                        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.k[dd][mt], qf[ks * (C::DS / 4) + dd],
-                                                                          sacc[mt], 0, 0, 0);
+                for (int dd = 0; dd < DPS; ++dd)
+                    sacc[KB][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        f.k[dd], qf[(ks % 2) * DPS + dd], (ks % 2 == 0 && dd == 0) ? f32x16{} : sacc[KB][mt], 0, 0,
+                        0);
             }
             if constexpr (PV) {
 #pragma unroll
@@ -517,12 +539,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
             }
         };
         __builtin_amdgcn_s_setprio(1);
-        if constexpr (QK) {
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) sacc[mt][e] = 0.f;
-        }
         using I0 = std::integral_constant<int, 0>;
         using I1 = std::integral_constant<int, 1>;
         using I2 = std::integral_constant<int, 2>;
@@ -530,15 +546,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
         Frag f0, f1;
         read(f0, I0{});
         read(f1, I1{});
-        mma(f0, I0{});
+        step(f0, I0{});
         __builtin_amdgcn_sched_barrier(0);
         read(f0, I2{});
-        mma(f1, I1{});
+        step(f1, I1{});
         __builtin_amdgcn_sched_barrier(0);
         read(f1, I3{});
-        mma(f0, I2{});
+        step(f0, I2{});
         __builtin_amdgcn_sched_barrier(0);
-        mma(f1, I3{});
+        step(f1, I3{});
+        if constexpr (PV) lsum += ls;
     };
 
     // A finished piece of pair pl of sequence b: the normalised output if the
@@ -596,12 +613,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
     bool prev_ends = false;
     int prev_b = 0, prev_pl = 0, prev_g = 0;
     // vector phase of tile i: close the piece that ended with tile i-1 (its last
-    // PV product ran in this tile's matrix phase), softmax of tile i, stage tile i+1
+    // softmax and PV product ran in this tile's matrix phase), mask and row max
+    // of tile i (the rescale it may call for applies before tile i's weights
+    // are added, in the next matrix phase), stage tile i+1
     auto vector = [&](auto P_, int i) __attribute__((always_inline)) {
         constexpr int P = decltype(P_)::value;  // i % 2
         __builtin_amdgcn_s_setprio(0);
         // my half of tile i+1 into LDS first: the writes complete while the
-        // softmax runs (its buffer was last read two intervals ago)
+        // rest of the phase runs (its buffer was last read two intervals ago)
         store(std::integral_constant<int, 1 - P>{}, i + 1);
         const bool close_prev = i > 0 && prev_ends;
         if (close_prev) epilogue(prev_b, prev_pl, prev_g, piece_t0 == 0);
@@ -622,13 +641,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                 for (int e = 0; e < 16; ++e)
-                    if (mt * 32 + (e >> 2) * 8 + (e & 3) >= lim) sacc[mt][e] = -INFINITY;
+                    if (mt * 32 + (e >> 2) * 8 + (e & 3) >= lim) sacc[P][mt][e] = -INFINITY;
         }
         float mx = -INFINITY;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[mt][e]);
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[P][mt][e]);
         const float mnew = max_with_partner(mx) * a.c_log2;
         const bool need = mnew > m2 + kTau;
         if (__builtin_amdgcn_ballot_w64(need)) {
@@ -640,19 +659,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
 #pragma unroll
                 for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
         }
-        const float neg = -m2;
-        float ls = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            f32x8 pv;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[ks >> 1][(ks & 1) * 8 + e], a.c_log2, neg));
-                ls += pv[e];
-            }
-            pf[ks] = __builtin_convertvector(pv, bf16x8);
-        }
-        lsum += ls;
         // next tile: its query rows if it starts a new piece (issued before the
         // staging loads, so waiting for them leaves those in flight), then the
         // loads of tile i+1+kNR
