@@ -5,10 +5,11 @@ Tolerances (attention, Nemotron-TwoTower Eq. 1):
   float32 path:  O max-abs <= 1e-5, LSE max-abs <= 1e-5
   bf16 path:     O max-abs <= 2e-2 and rel-L2 ||O - O_ref|| / ||O_ref|| <= 4e-3 over the
                  tensor; LSE max-abs <= 4e-3. The kernel rounds the softmax weights P
-                 to bf16 before the P.V product and normalises by the sum of the
-                 rounded weights, so LSE carries up to about 2^-9 relative error of
-                 that sum (the running max may trail the true max by up to 2^8, making
-                 the largest weight up to 256 before rounding); 4e-3 covers it twice.
+                 to bf16 before the P.V product and sums them in fp32 before that
+                 rounding, so O carries the bf16 rounding of P (about 2^-9 relative per
+                 weight) and LSE the fp32 summation error of up to a few thousand
+                 weights below 2^8 each (the running max may trail the true max by up
+                 to 2^8); 4e-3 covers both with margin.
 Confidence unmask (Algorithm 2): tokens, masks and counts bit-exact, except that a
 sequence is excluded when one of its decisions sits within 1e-6 of a threshold in the
 oracle's float64 values (a confidence within 1e-6 of gamma, or, on the fallback path,
