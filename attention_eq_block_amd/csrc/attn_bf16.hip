@@ -22,8 +22,8 @@
 // tiles of all pairs are laid end to end and cut into equal segments, one
 // per workgroup, so every CU streams the same number of tiles whatever the
 // spread of prefix lengths. A pair that lies inside one segment is written
-// directly; a pair cut by segment boundaries leaves one fp32 partial
-// (O normalised, LSE) per segment, merged by a second kernel. Segments are
+// directly; a pair cut by segment boundaries leaves one partial (O
+// normalised, in the output's precision, and its fp32 LSE) per segment, merged by a second kernel. Segments are
 // numbered so that consecutive ones run on the same XCD, which keeps a pair's
 // partials in one L2.
 //
@@ -597,14 +597,28 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
             }
             if (a.LSE && hl == 0) a.LSE[((long long)b * a.Hq + h) * a.S + s] = lse;
         } else {
+            // partial O in the output's precision: fp32 for an fp32 output, else bf16
             const long long slot = seg + b * mult + pl;
-            float* po = a.part_o + (slot * kRows + rl) * D + hl * 4;
+            const long long pe = (slot * kRows + rl) * D + hl * 4;
+            if (a.o_f32) {
+                float* po = a.part_o + pe;
 #pragma unroll
-            for (int dt = 0; dt < C::DT; ++dt)
+                for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    *reinterpret_cast<f32x4*>(po + dt * 32 + j * 8) =
-                        f32x4{oacc[dt][4 * j], oacc[dt][4 * j + 1], oacc[dt][4 * j + 2], oacc[dt][4 * j + 3]};
+                    for (int j = 0; j < 4; ++j)
+                        *reinterpret_cast<f32x4*>(po + dt * 32 + j * 8) =
+                            f32x4{oacc[dt][4 * j], oacc[dt][4 * j + 1], oacc[dt][4 * j + 2], oacc[dt][4 * j + 3]};
+            } else {
+                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                __bf16* po = reinterpret_cast<__bf16*>(a.part_o) + pe;
+#pragma unroll
+                for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        *reinterpret_cast<bf16x4*>(po + dt * 32 + j * 8) = __builtin_convertvector(
+                            (f32x4{oacc[dt][4 * j], oacc[dt][4 * j + 1], oacc[dt][4 * j + 2], oacc[dt][4 * j + 3]}),
+                            bf16x4);
+            }
             if (hl == 0) a.part_lse[slot * kRows + rl] = lse;
         }
     };
@@ -728,7 +742,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
 // Grid: n_pairs * 16 workgroups of 256 threads, 16 rows each; a row's 16
 // threads take D/16 consecutive floats each, and every partial a thread reads
 // is an independent load.
-template <int D>
+template <int D, bool F32>
 __global__ __launch_bounds__(kFinThreads) void attn_bf16_finalize(Args a, const int* __restrict__ ctx_len) {
     const int mult = a.Hkv * a.n_rb;
     const int p = blockIdx.x / 16, chunk = blockIdx.x % 16;
@@ -772,9 +786,18 @@ __global__ __launch_bounds__(kFinThreads) void attn_bf16_finalize(Args a, const 
             for (int j = 0; j < 4; ++j) {
                 const long long slot = min(sg0 + j, s1) + p;
                 l[j] = a.part_lse[slot * kRows + rl];
-                const float* po = a.part_o + (slot * kRows + rl) * D;
+                const long long pe = (slot * kRows + rl) * D;
 #pragma unroll
-                for (int k = 0; k < PER; ++k) v[j][k] = *reinterpret_cast<const f32x4*>(po + ((tid % 16) + 16 * k) * 4);
+                for (int k = 0; k < PER; ++k) {
+                    const int d = ((tid % 16) + 16 * k) * 4;
+                    if constexpr (F32) {
+                        v[j][k] = *reinterpret_cast<const f32x4*>(a.part_o + pe + d);
+                    } else {
+                        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                        v[j][k] = __builtin_convertvector(
+                            *reinterpret_cast<const bf16x4*>(reinterpret_cast<const __bf16*>(a.part_o) + pe + d), f32x4);
+                    }
+                }
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -860,11 +883,13 @@ tt_status launch_attn_bf16(const tt_block_attn_params& p, const AttnPlan& pl, vo
     if (p.head_dim == 128) {
         if (p2) hipLaunchKernelGGL((attn_bf16_kernel<128, true>), grid, blk, 0, s, a, a.page_table, a.ctx_len);
         else hipLaunchKernelGGL((attn_bf16_kernel<128, false>), grid, blk, 0, s, a, a.page_table, a.ctx_len);
-        hipLaunchKernelGGL(attn_bf16_finalize<128>, fgrid, fblk, 0, s, a, a.ctx_len);
+        if (a.o_f32) hipLaunchKernelGGL((attn_bf16_finalize<128, true>), fgrid, fblk, 0, s, a, a.ctx_len);
+        else hipLaunchKernelGGL((attn_bf16_finalize<128, false>), fgrid, fblk, 0, s, a, a.ctx_len);
     } else {
         if (p2) hipLaunchKernelGGL((attn_bf16_kernel<64, true>), grid, blk, 0, s, a, a.page_table, a.ctx_len);
         else hipLaunchKernelGGL((attn_bf16_kernel<64, false>), grid, blk, 0, s, a, a.page_table, a.ctx_len);
-        hipLaunchKernelGGL(attn_bf16_finalize<64>, fgrid, fblk, 0, s, a, a.ctx_len);
+        if (a.o_f32) hipLaunchKernelGGL((attn_bf16_finalize<64, true>), fgrid, fblk, 0, s, a, a.ctx_len);
+        else hipLaunchKernelGGL((attn_bf16_finalize<64, false>), fgrid, fblk, 0, s, a, a.ctx_len);
     }
     return hipGetLastError() == hipSuccess ? TT_OK : TT_ERR_HIP;
 }
