@@ -36,7 +36,9 @@
 // barrier interval behind group 0, so in every interval one wave on each SIMD
 // issues MFMAs while the other does the vector phase. Group 0 stages the K
 // half of every tile and group 1 the V half; each wave moves 16 keys of a
-// tile, so it needs one page id per tile.
+// tile, so it needs one page id per tile. The query rows of the next piece are
+// copied into LDS while the current one is computed, and a finished partial
+// is staged through the same LDS so that its stores write whole rows.
 #include <type_traits>
 
 #include "tt_internal.h"
@@ -324,6 +326,53 @@ __device__ __forceinline__ float sum_with_partner(float x) {
     return p0 + p1;
 }
 
+// The query fragments of a piece from their LDS copy (k-step ds of lane l at
+// addr + 1024 ds). Read in assembly, with the wait for the reads inside: the
+// copy was written by direct-to-LDS loads whose completion the caller has
+// already waited for, and the compiler, which cannot see that, would wait for
+// every load in flight before the reads.
+template <int DS>
+__device__ __forceinline__ void read_q_lds(bf16x8 (&qf)[DS], unsigned addr) {
+    u32x4 r[DS];
+    if constexpr (DS == 8) {
+        asm volatile(
+            "ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:1024\n\tds_read_b128 %2, %8 offset:2048\n\t"
+            "ds_read_b128 %3, %8 offset:3072\n\tds_read_b128 %4, %8 offset:4096\n\tds_read_b128 %5, %8 offset:5120\n\t"
+            "ds_read_b128 %6, %8 offset:6144\n\tds_read_b128 %7, %8 offset:7168\n\ts_waitcnt lgkmcnt(0)"
+            : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+            : "v"(addr)
+            : "memory");
+    } else {
+        static_assert(DS == 4, "");
+        asm volatile(
+            "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:1024\n\tds_read_b128 %2, %4 offset:2048\n\t"
+            "ds_read_b128 %3, %4 offset:3072\n\ts_waitcnt lgkmcnt(0)"
+            : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+            : "v"(addr)
+            : "memory");
+    }
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) qf[ds] = __builtin_bit_cast(bf16x8, r[ds]);
+}
+
+// Sixteen bytes per lane from each of four LDS addresses, and an 8-byte LDS
+// write: in assembly for the same reason (the buffer they use also receives
+// direct-to-LDS loads, none of them in flight when these run). The reads wait
+// for themselves and for every LDS access before them.
+__device__ __forceinline__ void lds_read_x4(u32x4 (&r)[4], const unsigned (&ad)[4]) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+        : "memory");
+}
+__device__ __forceinline__ void lds_write_b64(unsigned addr, unsigned lo, unsigned hi) {
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v = {lo, hi};
+    asm volatile("ds_write_b64 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+
 template <int D, bool P2>
 __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const int* __restrict__ page_table,
                                                                 const int* __restrict__ ctx_len) {
@@ -332,6 +381,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * C::KTILE + 2 * C::VTILE];
     __shared__ int sh[kThreads + 4];
     __shared__ int pgs[kWaves][2][64];  // page-id batches of each wave
+    // Query rows of the next piece, fetched ahead: wave w's 32 rows, lane l's
+    // 16 bytes of k-step ds at [w][1024 ds + 16 l]. Between pieces the same
+    // bytes stage a finished piece's bf16 rows (32 rows of pitch ROWB + 16).
+    __shared__ __attribute__((aligned(16))) uint8_t qlds[kWaves][C::DS * 1024 + 512];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -404,6 +457,24 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
                                                  idx * 4, 0, 0, 0);
     };
 
+    // Direct-to-LDS copy of the query rows of the piece at c (the fragments
+    // load_q would read, each lane's 16 bytes of step ds at qlds[wave][1024 ds +
+    // 16 lane]). It is issued when the load cursor enters the piece, kNR + 1
+    // tiles before the piece is computed, if the buffer is free.
+    auto q_dma = [&](const Cur& c) __attribute__((always_inline)) {
+        const int rb = c.pl - c.g * a.n_rb;
+        const int rr = min(rb * kRows + wave * 32 + l32, a.S * a.G - 1);
+        const int s = rr / a.G, h = c.g * a.G + rr % a.G;
+        const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(a.Q + (long long)c.b * a.qsb), (short)0, 0x7FFFFFFF, 0x00020000);
+        const int off = (s * a.qss + h * a.qsh + hl * 8) * 2;
+#pragma unroll
+        for (int ds = 0; ds < C::DS; ++ds)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (__attribute__((address_space(3))) void*)&qlds[wave][ds * 1024], 16,
+                                                     off + ds * 32, 0, 0, 0);
+    };
+    int q_tag = -1;  // segment index of the piece start whose rows are in qlds (-1: none)
+
     // Load pipeline: tile j's registers are filled kNR tiles before they are
     // stored. Every issue loads a whole tile (past the segment's end it reloads
     // the last one), so the wait counts the compiler derives are exact and
@@ -433,6 +504,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
         if (ul + 1 < n) {
             advance(cl, a, ctx_len);
             ++ul;
+            if (cl.t == 0 && q_tag < 0) {
+                q_dma(cl);
+                q_tag = ul;
+            }
         }
     };
 #pragma unroll
@@ -566,12 +641,57 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
         const float inv = 1.f / lt;
         const float lse = (m2 + __log2f(lt)) * kLn2;
         const int rl = wave * 32 + l32;  // row within the block
-        const int rr = (pl - g * a.n_rb) * kRows + rl;
-        if (rr >= a.S * a.G) return;
+        const int rb = pl - g * a.n_rb;
+        const int rr = rb * kRows + rl;
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
             for (int e = 0; e < 16; ++e) oacc[dt][e] *= inv;
+        if (!full && !a.o_f32 && q_tag < 0) {
+            // A partial in bf16: the rows go through this wave's query buffer (its
+            // rows have been read and no copy is in flight), so that every store
+            // writes whole rows (a lane holds 8-byte pieces of one row). The lane
+            // index is re-read here so that no per-lane address is kept live
+            // across the loop; the padded pitch spreads the writes over the banks.
+            unsigned ln;
+            asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+            constexpr int SP = C::ROWB + 16;
+            const unsigned qb = (unsigned)(uintptr_t)&qlds[wave][0];
+            const unsigned wa = qb + (ln & 31) * SP + ((ln >> 5) << 3);
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+                    const u32x2 v = __builtin_bit_cast(
+                        u32x2, __builtin_convertvector((f32x4{oacc[dt][4 * j], oacc[dt][4 * j + 1], oacc[dt][4 * j + 2],
+                                                              oacc[dt][4 * j + 3]}),
+                                                       bf16x4));
+                    lds_write_b64(wa + ((4 * dt + j) << 4), v[0], v[1]);
+                }
+            // lane l now takes chunk l % CPR of rows RPI*k + l / CPR; a wave's 32
+            // rows of the slot are 32*D contiguous elements
+            constexpr int NK = 32 / C::RPI;
+            const unsigned ra0 = qb + (ln / C::CPR) * SP + ((ln % C::CPR) << 4);
+            const long long slot = seg + b * mult + pl;
+            char* const po = reinterpret_cast<char*>(a.part_o) + (slot * kRows + wave * 32) * (D * 2);
+#pragma unroll
+            for (int k0 = 0; k0 < NK; k0 += 4) {
+                unsigned ra[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) ra[k] = ra0 + C::RPI * (k0 + k) * SP;
+                u32x4 v[4];
+                lds_read_x4(v, ra);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4*>(po + (ln * 16 + (k0 + k) * 1024)) = v[k];
+            }
+            if ((ln >> 5) == 0 && (rb * kRows + wave * 32 + (int)(ln & 31)) < a.S * a.G)
+                *reinterpret_cast<float*>(reinterpret_cast<char*>(a.part_lse) + (slot * kRows + wave * 32) * 4 +
+                                          (ln & 31) * 4) = lse;
+            return;
+        }
+        if (rr >= a.S * a.G) return;
         // lane holds d = 32*dt + 8*j + 4*hl + (0..3) in oacc[dt][4j .. 4j+3]
         if (full) {
             const int s = rr / a.G, h = g * a.G + rr % a.G;
@@ -683,10 +803,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
         if (i + 1 < n) {
             advance(cc, a, ctx_len);
             if (cc.t == 0) {
-                // waited for here, once per piece: left pending, the wait
-                // would sit before every tile's score MFMAs
-                load_q(cc);
-                __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+                if (q_tag == i + 1) {
+                    // the copy was issued before the loads of tile i+1, which were
+                    // waited for when that tile was staged at the start of this
+                    // phase, and loads complete in order
+                    read_q_lds(qf, (unsigned)(uintptr_t)&qlds[wave][lane * 16]);
+                    q_tag = -1;
+                } else {
+                    // waited for here, once per piece: left pending, the wait
+                    // would sit before every tile's score MFMAs
+                    load_q(cc);
+                    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+                }
             }
         }
         issue(R[(1 - P) % kNR]);
