@@ -120,55 +120,53 @@ __device__ __forceinline__ int seq_len(const Args& a, const int* __restrict__ ct
 }
 __device__ __forceinline__ int units_for(const Args& a, int L) { return (L + kTile - 1) / kTile + a.has_den; }
 
-// Block-wide, one pass over ctx_len: total units W and, for segment `seg` of
-// n_seg equal segments, its first unit u0, the sequence b0 holding it and the
-// first unit c0 of that sequence; with `before` set, also W and every
-// sequence's first unit there. `sh` is LDS scratch of NTHR + 4 ints.
-template <int NTHR>
-__device__ void scan_segment(const Args& a, const int* __restrict__ ctx_len, int seg, int* sh, int& W, int& u0,
-                             int& b0, int& c0, int* before) {
-    const int t = threadIdx.x;
+// Inclusive prefix sum over the 64 lanes of a wave
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+// Per wave, with no LDS or barrier (every wave of the block gets the same
+// result): total units W and, for segment `seg` of n_seg equal segments, its
+// first unit u0, the sequence b0 holding it and the first unit c0 of that
+// sequence; with `before` set, also W and every sequence's first unit there.
+// ctx_len is read 64 sequences at a time.
+__device__ void scan_segment(const Args& a, const int* __restrict__ ctx_len, int seg, int& W, int& u0, int& b0,
+                             int& c0, int* before) {
+    const int lane = threadIdx.x & 63;
     const int mult = a.Hkv * a.n_rb;
-    const int chunk = (a.B + NTHR - 1) / NTHR;
-    const int lo = min(a.B, t * chunk), hi = min(a.B, lo + chunk);
-    int sum = 0;
-    for (int b = lo; b < hi; ++b) sum += units_for(a, ctx_len ? clamp_len(ctx_len[b], a.Lmax) : 0) * mult;
-    sh[t] = sum;
-    __syncthreads();
-    for (int off = 1; off < NTHR; off <<= 1) {
-        const int v = t >= off ? sh[t - off] : 0;
-        __syncthreads();
-        sh[t] += v;
-        __syncthreads();
-    }
-    const int incl = sh[t];
-    const int excl = incl - sum;
-    W = sh[NTHR - 1];
-    if (before) {
-        if (t == 0) before[0] = W;
-        int c = excl;
-        for (int b = lo; b < hi; ++b) {
-            before[1 + b] = c;
-            c += units_for(a, ctx_len ? clamp_len(ctx_len[b], a.Lmax) : 0) * mult;
-        }
-    }
+    auto units_at = [&](int b) {
+        return b < a.B ? units_for(a, ctx_len ? clamp_len(ctx_len[b], a.Lmax) : 0) * mult : 0;
+    };
+    const int n0 = units_at(lane);
+    int w = 0;
+    for (int base = 0; base < a.B; base += 64)
+        w += __builtin_amdgcn_readlane(wave_incl_scan(base == 0 ? n0 : units_at(base + lane), lane), 63);
+    W = w;
     const int seg_len = (W + a.n_seg - 1) / a.n_seg;
     u0 = seg * seg_len;
-    __syncthreads();
-    if (t == 0) { sh[NTHR] = 0; sh[NTHR + 1] = 0; }
-    __syncthreads();
-    if (u0 >= excl && u0 < incl) {
-        int c = excl;
-        for (int b = lo; b < hi; ++b) {
-            const int n = units_for(a, ctx_len ? clamp_len(ctx_len[b], a.Lmax) : 0) * mult;
-            if (u0 < c + n) { sh[NTHR] = b; sh[NTHR + 1] = c; break; }
-            c += n;
+    b0 = 0;
+    c0 = 0;
+    int carry = 0;
+    for (int base = 0; base < a.B; base += 64) {
+        const int nb = base == 0 ? n0 : units_at(base + lane);
+        const int incl = carry + wave_incl_scan(nb, lane);
+        const int excl = incl - nb;
+        if (before && base + lane < a.B) before[1 + base + lane] = excl;
+        const unsigned long long hit = __builtin_amdgcn_ballot_w64(nb > 0 && u0 >= excl && u0 < incl);
+        if (hit) {
+            const int l = __builtin_ctzll(hit);
+            b0 = base + l;
+            c0 = __builtin_amdgcn_readlane(excl, l);
+            if (!before) break;
         }
+        carry = __builtin_amdgcn_readlane(incl, 63);
     }
-    __syncthreads();
-    b0 = sh[NTHR];
-    c0 = sh[NTHR + 1];
-    __syncthreads();
+    if (before && lane == 0) before[0] = W;
 }
 
 // Position in the tile stream. Pair pl of sequence b is (kv head g, row block
@@ -379,7 +377,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
     using C = Cfg<D>;
     // K tiles (two buffers), then V tiles (two buffers)
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * C::KTILE + 2 * C::VTILE];
-    __shared__ int sh[kThreads + 4];
     __shared__ int pgs[kWaves][2][64];  // page-id batches of each wave
     // Query rows of the next piece, fetched ahead: wave w's 32 rows, lane l's
     // 16 bytes of k-step ds at [w][1024 ds + 16 l]. Between pieces the same
@@ -397,7 +394,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
     const int seg = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
 
     int W, u0, b0, c0;
-    scan_segment<kThreads>(a, ctx_len, seg, sh, W, u0, b0, c0, seg == 0 ? a.units_before : nullptr);
+    scan_segment(a, ctx_len, seg, W, u0, b0, c0, seg == 0 && wave == 0 ? a.units_before : nullptr);
     W = __builtin_amdgcn_readfirstlane(W);
     u0 = __builtin_amdgcn_readfirstlane(u0);
     const int seg_len = (W + a.n_seg - 1) / a.n_seg;
@@ -510,8 +507,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
             }
         }
     };
-#pragma unroll
-    for (int k = 0; k < kNR; ++k) issue(R[k]);
     // Tile j's registers are R[j % kNR]: stored to LDS buffer j % 2, then
     // refilled with tile j + kNR.
     auto store = [&](auto J_, int j) __attribute__((always_inline)) {
@@ -820,9 +815,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
         issue(R[(1 - P) % kNR]);
     };
 
-    // ---- prologue: group 0 stages K of tile 0 before the first barrier, group 1
-    // stages V of tile 0 in the first interval ----
+    // ---- prologue: the loads of the first tile, the query rows, the loads of
+    // the tiles after (so the rows arrive with the first tile); group 0 stages
+    // K of tile 0 before the first barrier, group 1 stages V of tile 0 in the
+    // first interval ----
+    issue(R[0]);
     load_q(cc);
+#pragma unroll
+    for (int k = 1; k < kNR; ++k) issue(R[k]);
     if (grp == 0) feed(std::integral_constant<int, 0>{}, 0);
     lds_barrier();
     if (grp == 1) {
