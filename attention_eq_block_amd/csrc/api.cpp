@@ -75,10 +75,10 @@ tt_status validate_attn(const tt_block_attn_params* p) {
             !stride_ok(p->den_stride_h, p->dtype))
             return TT_ERR_UNSUPPORTED;
     }
-    // the bf16 path counts tiles in 32-bit integers
+    // the bf16 path counts tiles (and the piece-start charge) in 32-bit integers
     const int64_t G = p->Hq / p->Hkv;
     const int64_t n_rb = (p->S * G + tt::kRows - 1) / tt::kRows;
-    const int64_t tiles = ((int64_t)p->max_ctx_len + tt::kTile - 1) / tt::kTile + 1;
+    const int64_t tiles = ((int64_t)p->max_ctx_len + tt::kTile - 1) / tt::kTile + 1 + tt::kPieceCost;
     if ((int64_t)p->B * p->Hkv * n_rb * tiles >= (int64_t)1 << 30) return TT_ERR_SHAPE;
     return TT_OK;
 }

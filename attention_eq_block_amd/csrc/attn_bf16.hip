@@ -19,9 +19,9 @@
 //
 // Work split. The prefix of each (sequence, kv head, row block) "pair" is cut
 // into 64-key tiles, followed by one tile holding the S block keys. All
-// tiles of all pairs are laid end to end and cut into equal segments, one
-// per workgroup, so every CU streams the same number of tiles whatever the
-// spread of prefix lengths. A pair that lies inside one segment is written
+// tiles of all pairs are laid end to end and cut into segments of equal cost
+// (tiles, plus a fixed charge for every piece start), one per workgroup, so
+// every CU does the same work whatever the spread of prefix lengths. A pair that lies inside one segment is written
 // directly; a pair cut by segment boundaries leaves one partial (O
 // normalised, in the output's precision, and its fp32 LSE) per segment, merged by a second kernel. Segments are
 // numbered so that consecutive ones run on the same XCD, which keeps a pair's
@@ -61,6 +61,7 @@ constexpr int kNR = TT_ATTN_PREFETCH;      // tiles in flight in registers per w
 constexpr int kThreads = 64 * kWaves;
 constexpr int kFinThreads = 256;
 constexpr float kTau = 8.0f;  // lazy rescale threshold (log2 units)
+
 constexpr float kLn2 = 0.693147180559945309f;
 static_assert(kRows == 32 * kWaves, "one 32-row MFMA tile per wave");
 
@@ -107,8 +108,9 @@ struct Args {
     float* LSE;
     float* part_o;
     float* part_lse;
-    int* units_before;  // [0]: total units W; [1 + b]: units of the sequences before b
+    int* units_before;  // [0]: total weighted units W; [1 + b]: weighted units of the sequences before b
     int B, S, Hq, Hkv, G, n_rb, has_den, n_seg;
+    int pe;  // extra units counted at the start of every pair (its piece-start cost)
     float c_log2;  // softmax_scale * log2(e)
 };
 
@@ -130,43 +132,64 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
     return x;
 }
 
+// Segments are cut by weighted units: every pair with tiles counts its tiles
+// plus pe extra units before its first tile, the cost of starting a piece
+// (query rows, the epilogue of the piece before), so that a segment holding
+// piece starts gets fewer tiles. Tile t of a pair that starts at weighted unit
+// V sits at V + pe + t.
+//
 // Per wave, with no LDS or barrier (every wave of the block gets the same
-// result): total units W and, for segment `seg` of n_seg equal segments, its
-// first unit u0, the sequence b0 holding it and the first unit c0 of that
-// sequence; with `before` set, also W and every sequence's first unit there.
-// ctx_len is read 64 sequences at a time.
-__device__ void scan_segment(const Args& a, const int* __restrict__ ctx_len, int seg, int& W, int& u0, int& b0,
-                             int& c0, int* before) {
+// result): the tiles of segment `seg`, n of them from tile t0 of pair pl0 of
+// sequence b0; with `before` set, also the total weighted units and every
+// sequence's first weighted unit there. ctx_len is read 64 sequences at a time.
+__device__ void scan_segment(const Args& a, const int* __restrict__ ctx_len, int seg, int& n, int& b0, int& pl0,
+                             int& t0, int* before) {
     const int lane = threadIdx.x & 63;
     const int mult = a.Hkv * a.n_rb;
-    auto units_at = [&](int b) {
-        return b < a.B ? units_for(a, ctx_len ? clamp_len(ctx_len[b], a.Lmax) : 0) * mult : 0;
+    auto units_at = [&](int b) {  // tiles per pair of sequence b
+        return b < a.B ? units_for(a, ctx_len ? clamp_len(ctx_len[b], a.Lmax) : 0) : 0;
     };
-    const int n0 = units_at(lane);
-    int w = 0;
+    auto weighted = [&](int u) { return u > 0 ? mult * (u + a.pe) : 0; };
+    const int u_first = units_at(lane);
+    int wv = 0;
     for (int base = 0; base < a.B; base += 64)
-        w += __builtin_amdgcn_readlane(wave_incl_scan(base == 0 ? n0 : units_at(base + lane), lane), 63);
-    W = w;
-    const int seg_len = (W + a.n_seg - 1) / a.n_seg;
-    u0 = seg * seg_len;
-    b0 = 0;
-    c0 = 0;
-    int carry = 0;
+        wv += __builtin_amdgcn_readlane(wave_incl_scan(weighted(base == 0 ? u_first : units_at(base + lane)), lane), 63);
+    const int len = (wv + a.n_seg - 1) / a.n_seg;
+    const int x0 = seg * len, x1 = min(wv, x0 + len);
+    // r0, r1: tiles before weighted units x0 and x1
+    int r0 = -1, r1 = -1;
+    b0 = pl0 = t0 = 0;
+    int vcarry = 0, rcarry = 0;
     for (int base = 0; base < a.B; base += 64) {
-        const int nb = base == 0 ? n0 : units_at(base + lane);
-        const int incl = carry + wave_incl_scan(nb, lane);
-        const int excl = incl - nb;
-        if (before && base + lane < a.B) before[1 + base + lane] = excl;
-        const unsigned long long hit = __builtin_amdgcn_ballot_w64(nb > 0 && u0 >= excl && u0 < incl);
-        if (hit) {
-            const int l = __builtin_ctzll(hit);
+        const int u = base == 0 ? u_first : units_at(base + lane);
+        const int vu = weighted(u);
+        const int vincl = vcarry + wave_incl_scan(vu, lane), vexcl = vincl - vu;
+        const int rincl = rcarry + wave_incl_scan(mult * u, lane), rexcl = rincl - mult * u;
+        if (before && base + lane < a.B) before[1 + base + lane] = vexcl;
+        const unsigned long long h0 = __builtin_amdgcn_ballot_w64(vu > 0 && x0 >= vexcl && x0 < vincl);
+        if (h0) {
+            const int l = __builtin_ctzll(h0);
+            const int ub = __builtin_amdgcn_readlane(u, l);
+            const int off = x0 - __builtin_amdgcn_readlane(vexcl, l);
             b0 = base + l;
-            c0 = __builtin_amdgcn_readlane(excl, l);
-            if (!before) break;
+            pl0 = off / (ub + a.pe);
+            t0 = max(off % (ub + a.pe) - a.pe, 0);
+            r0 = __builtin_amdgcn_readlane(rexcl, l) + pl0 * ub + t0;
         }
-        carry = __builtin_amdgcn_readlane(incl, 63);
+        const unsigned long long h1 = __builtin_amdgcn_ballot_w64(vu > 0 && x1 >= vexcl && x1 < vincl);
+        if (h1) {
+            const int l = __builtin_ctzll(h1);
+            const int ub = __builtin_amdgcn_readlane(u, l);
+            const int off = x1 - __builtin_amdgcn_readlane(vexcl, l);
+            r1 = __builtin_amdgcn_readlane(rexcl, l) + (off / (ub + a.pe)) * ub + max(off % (ub + a.pe) - a.pe, 0);
+        }
+        vcarry = __builtin_amdgcn_readlane(vincl, 63);
+        rcarry = __builtin_amdgcn_readlane(rincl, 63);
+        if (r1 >= 0 && !before) break;
     }
-    if (before && lane == 0) before[0] = W;
+    if (r1 < 0) r1 = rcarry;  // x1 is the end of the stream
+    n = r0 < 0 ? 0 : r1 - r0;
+    if (before && lane == 0) before[0] = wv;
 }
 
 // Position in the tile stream. Pair pl of sequence b is (kv head g, row block
@@ -393,23 +416,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
     const int per_xcd = a.n_seg / 8;
     const int seg = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
 
-    int W, u0, b0, c0;
-    scan_segment(a, ctx_len, seg, W, u0, b0, c0, seg == 0 && wave == 0 ? a.units_before : nullptr);
-    W = __builtin_amdgcn_readfirstlane(W);
-    u0 = __builtin_amdgcn_readfirstlane(u0);
-    const int seg_len = (W + a.n_seg - 1) / a.n_seg;
-    const int n = min(W, u0 + seg_len) - u0;  // tiles of this segment
+    int n, b0, pl0, t0;  // tiles of this segment, from tile t0 of pair pl0 of sequence b0
+    scan_segment(a, ctx_len, seg, n, b0, pl0, t0, seg == 0 && wave == 0 ? a.units_before : nullptr);
+    n = __builtin_amdgcn_readfirstlane(n);
     if (n <= 0) return;
     b0 = __builtin_amdgcn_readfirstlane(b0);
-    c0 = __builtin_amdgcn_readfirstlane(c0);
+    pl0 = __builtin_amdgcn_readfirstlane(pl0);
+    t0 = __builtin_amdgcn_readfirstlane(t0);
 
     Cur cc;  // tile being computed
     set_seq(cc, a, ctx_len, b0);
-    {
-        const int off = u0 - c0;
-        set_pair(cc, a, off / cc.units);
-        cc.t = off % cc.units;
-    }
+    set_pair(cc, a, pl0);
+    cc.t = t0;
     const int mult = a.Hkv * a.n_rb;
 
     // ---- this group's half of every tile ----
@@ -881,7 +899,8 @@ __global__ __launch_bounds__(kFinThreads) void attn_bf16_finalize(Args a, const 
     const int seg_len = (W + a.n_seg - 1) / a.n_seg;
     int s0 = 0, s1 = -1;
     if (units > 0) {
-        const int U = a.units_before[1 + b] + pl * units;
+        // weighted unit of the pair's first tile
+        const int U = a.units_before[1 + b] + pl * (units + a.pe) + a.pe;
         s0 = U / seg_len;
         s1 = (U + units - 1) / seg_len;
         if (s0 == s1) return;  // written by the main kernel
@@ -1000,6 +1019,7 @@ tt_status launch_attn_bf16(const tt_block_attn_params& p, const AttnPlan& pl, vo
     a.n_rb = pl.n_rb;
     a.has_den = p.Kden ? 1 : 0;
     a.n_seg = pl.n_seg;
+    a.pe = kPieceCost;
     a.c_log2 = p.softmax_scale * 1.44269504088896340736f;
     a.page_shift = -1;
     if (p.page_size > 0 && (p.page_size & (p.page_size - 1)) == 0) {

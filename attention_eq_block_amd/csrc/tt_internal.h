@@ -14,11 +14,16 @@ namespace tt {
 // One "pair" is (sequence b, kv head g, row block rb): the S*G query rows that
 // share kv head g, cut into blocks of kRows rows. The key stream of a pair is
 // its prefix in tiles of kTile keys followed by one tile of the S block keys.
-// All pairs' tiles, laid end to end, are cut into n_seg equal segments, one
-// per workgroup (stream-K); a pair cut by a segment boundary is finished by a
+// All pairs' tiles, laid end to end, are cut into n_seg segments of equal
+// cost, one per workgroup (stream-K): a pair costs its tiles plus kPieceCost
+// for starting a piece. A pair cut by a segment boundary is finished by a
 // log-sum-exp merge of the per-segment partials.
 constexpr int kTile = 64;   // keys per tile
-constexpr int kRows = 256;  // query rows per workgroup (4 waves x 64 rows)
+constexpr int kRows = 256;  // query rows per workgroup (8 waves x 32 rows)
+#ifndef TT_PIECE_COST
+#define TT_PIECE_COST 3
+#endif
+constexpr int kPieceCost = TT_PIECE_COST;  // in tiles, measured on long prefixes
 
 struct AttnPlan {
     int n_rb;      // row blocks per (b, g)
