@@ -347,13 +347,24 @@ __device__ __forceinline__ float sum_with_partner(float x) {
     return p0 + p1;
 }
 
+// This lane's index, computed where it is used: a value the compiler cannot
+// hoist, so no per-lane address derived from it stays live across a loop
+// (where it could be spilled, and the reload would wait for every load in
+// flight).
+__device__ __forceinline__ unsigned lane_here() {
+    unsigned ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    return ln;
+}
+
 // The query fragments of a piece from their LDS copy (k-step ds of lane l at
-// addr + 1024 ds). Read in assembly, with the wait for the reads inside: the
-// copy was written by direct-to-LDS loads whose completion the caller has
-// already waited for, and the compiler, which cannot see that, would wait for
-// every load in flight before the reads.
+// base + 16 l + 1024 ds). Read in assembly, with the wait for the reads
+// inside: the copy was written by direct-to-LDS loads whose completion the
+// caller has already waited for, and the compiler, which cannot see that,
+// would wait for every load in flight before the reads.
 template <int DS>
-__device__ __forceinline__ void read_q_lds(bf16x8 (&qf)[DS], unsigned addr) {
+__device__ __forceinline__ void read_q_lds(bf16x8 (&qf)[DS], unsigned base) {
+    const unsigned addr = base + 16 * lane_here();
     u32x4 r[DS];
     if constexpr (DS == 8) {
         asm volatile(
@@ -477,12 +488,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
     // 16 lane]). It is issued when the load cursor enters the piece, kNR + 1
     // tiles before the piece is computed, if the buffer is free.
     auto q_dma = [&](const Cur& c) __attribute__((always_inline)) {
+        const unsigned ln = lane_here();
         const int rb = c.pl - c.g * a.n_rb;
-        const int rr = min(rb * kRows + wave * 32 + l32, a.S * a.G - 1);
+        const int rr = min(rb * kRows + wave * 32 + (int)(ln & 31), a.S * a.G - 1);
         const int s = rr / a.G, h = c.g * a.G + rr % a.G;
         const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(a.Q + (long long)c.b * a.qsb), (short)0, 0x7FFFFFFF, 0x00020000);
-        const int off = (s * a.qss + h * a.qsh + hl * 8) * 2;
+        const int off = (s * a.qss + h * a.qsh + (int)(ln >> 5) * 8) * 2;
 #pragma unroll
         for (int ds = 0; ds < C::DS; ++ds)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (__attribute__((address_space(3))) void*)&qlds[wave][ds * 1024], 16,
@@ -552,10 +564,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
 
     // query rows of the pair at c (a row past S*G reads the last row; it is never written)
     auto load_q = [&](const Cur& c) __attribute__((always_inline)) {
+        const unsigned ln = lane_here();
         const int rb = c.pl - c.g * a.n_rb;
-        const int rr = min(rb * kRows + wave * 32 + l32, a.S * a.G - 1);
+        const int rr = min(rb * kRows + wave * 32 + (int)(ln & 31), a.S * a.G - 1);
         const int s = rr / a.G, h = c.g * a.G + rr % a.G;
-        const uint16_t* q = a.Q + (long long)c.b * a.qsb + (long long)s * a.qss + (long long)h * a.qsh + hl * 8;
+        const uint16_t* q =
+            a.Q + (long long)c.b * a.qsb + (long long)s * a.qss + (long long)h * a.qsh + (int)(ln >> 5) * 8;
 #pragma unroll
         for (int ds = 0; ds < C::DS; ++ds) qf[ds] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q + ds * 16));
     };
@@ -663,11 +677,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
         if (!full && !a.o_f32 && q_tag < 0) {
             // A partial in bf16: the rows go through this wave's query buffer (its
             // rows have been read and no copy is in flight), so that every store
-            // writes whole rows (a lane holds 8-byte pieces of one row). The lane
-            // index is re-read here so that no per-lane address is kept live
-            // across the loop; the padded pitch spreads the writes over the banks.
-            unsigned ln;
-            asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+            // writes whole rows (a lane holds 8-byte pieces of one row). The
+            // padded pitch spreads the writes over the banks.
+            const unsigned ln = lane_here();
             constexpr int SP = C::ROWB + 16;
             const unsigned qb = (unsigned)(uintptr_t)&qlds[wave][0];
             const unsigned wa = qb + (ln & 31) * SP + ((ln >> 5) << 3);
@@ -820,7 +832,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
                     // the copy was issued before the loads of tile i+1, which were
                     // waited for when that tile was staged at the start of this
                     // phase, and loads complete in order
-                    read_q_lds(qf, (unsigned)(uintptr_t)&qlds[wave][lane * 16]);
+                    read_q_lds(qf, (unsigned)(uintptr_t)&qlds[wave][0]);
                     q_tag = -1;
                 } else {
                     // waited for here, once per piece: left pending, the wait
