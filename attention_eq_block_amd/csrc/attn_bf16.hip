@@ -116,6 +116,11 @@ struct Args {
 
 typedef __attribute__((address_space(4))) const int const_int;
 
+// branch weights for the block-frequency estimates the register allocator
+// uses: the rare paths (piece ends, ragged tails, batch refills) are cold
+#define TT_LIKELY(x) __builtin_expect(!!(x), 1)
+#define TT_UNLIKELY(x) __builtin_expect(!!(x), 0)
+
 // ctx_len is read through the constant address space: scalar loads
 __device__ __forceinline__ int seq_len(const Args& a, const int* __restrict__ ctx_len, int b) {
     return ctx_len ? clamp_len(((const_int*)ctx_len)[b], a.Lmax) : 0;
@@ -215,7 +220,7 @@ __device__ __forceinline__ void set_pair(Cur& c, const Args& a, int pl) {
 }
 
 __device__ __forceinline__ void advance(Cur& c, const Args& a, const int* __restrict__ ctx_len) {
-    if (++c.t < c.units) return;
+    if (TT_LIKELY(++c.t < c.units)) return;
     c.t = 0;
     if (c.pl + 1 < a.Hkv * a.n_rb) {
         set_pair(c, a, c.pl + 1);
@@ -263,14 +268,14 @@ __device__ __forceinline__ void load_tile(Regs<D>& r, const Cur& c, int page, co
     const int ch = lane % C::CPR, lrow = lane / C::CPR;
     const char* base;
     unsigned off[C::LPG];
-    if (is_prefix(c, a)) {
+    if (TT_LIKELY(is_prefix(c, a))) {
         int j0 = c.t * kTile + 16 * wq;
-        if (j0 >= c.L) j0 = (c.L - 1) & ~15;
+        if (TT_UNLIKELY(j0 >= c.L)) j0 = (c.L - 1) & ~15;
         const int last = c.L - 1 - j0;  // rows 0..last of the block are keys
         page = min(max(page, 0), a.num_pages - 1);
         base = reinterpret_cast<const char*>(src_c + (((long long)page * a.Hkv + c.g) * a.page_size +
                                                       slot_of<P2>(a, j0)) * D);
-        if (last >= 15) {
+        if (TT_LIKELY(last >= 15)) {
 #pragma unroll
             for (int i = 0; i < C::LPG; ++i) off[i] = loff + (unsigned)(C::RPI * i * D * 2);
         } else {
@@ -519,7 +524,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): both batches have landed
     int pgl = pgs[wave][0][lane];
     auto issue = [&](Regs<D>& r) __attribute__((always_inline)) {
-        if (ul - pg_base == 64) {
+        if (TT_UNLIKELY(ul - pg_base == 64)) {
             pg_base = ul;
             pbuf ^= 1;
             pgl = pgs[wave][pbuf][lane];
@@ -531,7 +536,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
         if (ul + 1 < n) {
             advance(cl, a, ctx_len);
             ++ul;
-            if (cl.t == 0 && q_tag < 0) {
+            if (TT_UNLIKELY(cl.t == 0 && q_tag < 0)) {
                 q_dma(cl);
                 q_tag = ul;
             }
@@ -541,7 +546,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
     // refilled with tile j + kNR.
     auto store = [&](auto J_, int j) __attribute__((always_inline)) {
         constexpr int J = decltype(J_)::value;  // j % 2
-        if (j < n) store_tile<D>(R[J % kNR], mybuf + J * mytile, mypitch, wq, lane);
+        if (TT_LIKELY(j < n)) store_tile<D>(R[J % kNR], mybuf + J * mytile, mypitch, wq, lane);
     };
     auto feed = [&](auto J_, int j) __attribute__((always_inline)) {
         store(J_, j);
@@ -782,8 +787,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
         // rest of the phase runs (its buffer was last read two intervals ago)
         store(std::integral_constant<int, 1 - P>{}, i + 1);
         const bool close_prev = i > 0 && prev_ends;
-        if (close_prev) epilogue(prev_b, prev_pl, prev_g, piece_t0 == 0);
-        if (i == 0 || close_prev) {
+        if (TT_UNLIKELY(close_prev)) epilogue(prev_b, prev_pl, prev_g, piece_t0 == 0);
+        if (TT_UNLIKELY(i == 0 || close_prev)) {
             piece_t0 = cc.t;
             m2 = -INFINITY;
             lsum = 0.f;
@@ -793,7 +798,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
                 for (int e = 0; e < 16; ++e) oacc[dt][e] = 0.f;
         }
         const int nvalid = is_prefix(cc, a) ? min(kTile, cc.L - cc.t * kTile) : a.S;
-        if (nvalid < kTile) {
+        if (TT_UNLIKELY(nvalid < kTile)) {
             // key of element e of sacc[mt] is mt*32 + 8*(e/4) + e%4 + 4*hl
             const int lim = nvalid - 4 * hl;
 #pragma unroll
@@ -809,7 +814,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
             for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[P][mt][e]);
         const float mnew = max_with_partner(mx) * a.c_log2;
         const bool need = mnew > m2 + kTau;
-        if (__builtin_amdgcn_ballot_w64(need)) {
+        if (TT_UNLIKELY(__builtin_amdgcn_ballot_w64(need))) {
             const float alpha = need ? __builtin_amdgcn_exp2f(m2 - mnew) : 1.f;
             if (need) m2 = mnew;
             lsum *= alpha;
@@ -827,7 +832,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
         prev_g = cc.g;
         if (i + 1 < n) {
             advance(cc, a, ctx_len);
-            if (cc.t == 0) {
+            if (TT_UNLIKELY(cc.t == 0)) {
                 if (q_tag == i + 1) {
                     // the copy was issued before the loads of tile i+1, which were
                     // waited for when that tile was staged at the start of this
