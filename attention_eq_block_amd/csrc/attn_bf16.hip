@@ -903,8 +903,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
 // and write O = 0, LSE = -inf for pairs with no keys at all. The pair's
 // segments follow from the unit counts the main kernel left in the workspace.
 // Grid: n_pairs * 16 workgroups of 256 threads, 16 rows each; a row's 16
-// threads take D/16 consecutive floats each, and every partial a thread reads
-// is an independent load.
+// threads take D/16 consecutive elements each, and every partial a thread
+// reads is an independent load.
 template <int D, bool F32>
 __global__ __launch_bounds__(kFinThreads) void attn_bf16_finalize(Args a, const int* __restrict__ ctx_len) {
     const int mult = a.Hkv * a.n_rb;
@@ -928,61 +928,51 @@ __global__ __launch_bounds__(kFinThreads) void attn_bf16_finalize(Args a, const 
     if (rr >= a.S * a.G) return;
     const int s = rr / a.G, h = g * a.G + rr % a.G;
     const long long ob = (long long)b * a.osb + (long long)s * a.oss + (long long)h * a.osh;
-    // partials in groups of four, each group's loads issued together (an index
-    // past s1 rereads slot s1 and gets weight 0)
-    float M = -INFINITY;
+    // Partials in groups of four, the LSEs and rows of a group loaded together
+    // (an index past s1 rereads slot s1 and gets weight 0); the running max M
+    // and the sums are rescaled when a group raises M.
+    constexpr int EPT = D / 16;  // elements per thread
+    const int d0 = (tid % 16) * EPT;
+    typedef float f32xE __attribute__((ext_vector_type(EPT)));
+    typedef __bf16 bf16xE __attribute__((ext_vector_type(EPT)));
+    float M = -INFINITY, Wsum = 0.f;
+    f32xE acc = {};
     for (int sg0 = s0; sg0 <= s1; sg0 += 4) {
         float l[4];
+        f32xE v[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) l[j] = a.part_lse[(long long)(min(sg0 + j, s1) + p) * kRows + rl];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) M = fmaxf(M, l[j]);
-    }
-    constexpr int PER = D / 64;  // 4-float chunks per thread
-    f32x4 acc[PER];
-    for (int k = 0; k < PER; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float Wsum = 0.f;
-    if (M != -INFINITY) {
-        for (int sg0 = s0; sg0 <= s1; sg0 += 4) {
-            float l[4];
-            f32x4 v[4][PER];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const long long slot = min(sg0 + j, s1) + p;
-                l[j] = a.part_lse[slot * kRows + rl];
-                const long long pe = (slot * kRows + rl) * D;
-#pragma unroll
-                for (int k = 0; k < PER; ++k) {
-                    const int d = ((tid % 16) + 16 * k) * 4;
-                    if constexpr (F32) {
-                        v[j][k] = *reinterpret_cast<const f32x4*>(a.part_o + pe + d);
-                    } else {
-                        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-                        v[j][k] = __builtin_convertvector(
-                            *reinterpret_cast<const bf16x4*>(reinterpret_cast<const __bf16*>(a.part_o) + pe + d), f32x4);
-                    }
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float w = (sg0 + j <= s1 && l[j] != -INFINITY) ? __expf(l[j] - M) : 0.f;
-                Wsum += w;
-#pragma unroll
-                for (int k = 0; k < PER; ++k) acc[k] += w * v[j][k];
-            }
+        for (int j = 0; j < 4; ++j) {
+            const long long slot = min(sg0 + j, s1) + p;
+            l[j] = a.part_lse[slot * kRows + rl];
+            const long long pe = (slot * kRows + rl) * D + d0;
+            if constexpr (F32)
+                v[j] = *reinterpret_cast<const f32xE*>(a.part_o + pe);
+            else
+                v[j] = __builtin_convertvector(*reinterpret_cast<const bf16xE*>(reinterpret_cast<const __bf16*>(a.part_o) + pe),
+                                               f32xE);
         }
+        float mg = M;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (sg0 + j <= s1) mg = fmaxf(mg, l[j]);
+        if (mg == -INFINITY) continue;
+        const float sc = __expf(M - mg);  // 0 while M is -inf
+        Wsum *= sc;
+        acc *= sc;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float w = (sg0 + j <= s1 && l[j] != -INFINITY) ? __expf(l[j] - mg) : 0.f;
+            Wsum += w;
+            acc += w * v[j];
+        }
+        M = mg;
     }
     const float inv = Wsum > 0.f ? 1.f / Wsum : 0.f;
-    for (int k = 0; k < PER; ++k) {
-        const int d = ((tid % 16) + 16 * k) * 4;
-        const f32x4 o = acc[k] * inv;
-        if (a.o_f32) {
-            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.O) + ob + d) = o;
-        } else {
-            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-            *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(a.O) + ob + d) = __builtin_convertvector(o, bf16x4);
-        }
-    }
+    const f32xE o = acc * inv;
+    if (a.o_f32)
+        *reinterpret_cast<f32xE*>(reinterpret_cast<float*>(a.O) + ob + d0) = o;
+    else
+        *reinterpret_cast<bf16xE*>(reinterpret_cast<__bf16*>(a.O) + ob + d0) = __builtin_convertvector(o, bf16xE);
     if (a.LSE && tid % 16 == 0)
         a.LSE[((long long)b * a.Hq + h) * a.S + s] = Wsum > 0.f ? M + __logf(Wsum) : -INFINITY;
 }
