@@ -929,17 +929,16 @@ __global__ __launch_bounds__(kFinThreads) void attn_bf16_finalize(Args a, const 
     const int s = rr / a.G, h = g * a.G + rr % a.G;
     const long long ob = (long long)b * a.osb + (long long)s * a.oss + (long long)h * a.osh;
     // Partials in groups of four, the LSEs and rows of a group loaded together
-    // (an index past s1 rereads slot s1 and gets weight 0); the running max M
-    // and the sums are rescaled when a group raises M.
+    // (an index past s1 rereads slot s1 and gets weight 0) and the next group
+    // loaded while one is merged; the running max M and the sums are rescaled
+    // when a group raises M.
     constexpr int EPT = D / 16;  // elements per thread
     const int d0 = (tid % 16) * EPT;
     typedef float f32xE __attribute__((ext_vector_type(EPT)));
     typedef __bf16 bf16xE __attribute__((ext_vector_type(EPT)));
     float M = -INFINITY, Wsum = 0.f;
     f32xE acc = {};
-    for (int sg0 = s0; sg0 <= s1; sg0 += 4) {
-        float l[4];
-        f32xE v[4];
+    auto load = [&](int sg0, float (&l)[4], f32xE (&v)[4]) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const long long slot = min(sg0 + j, s1) + p;
@@ -948,14 +947,16 @@ __global__ __launch_bounds__(kFinThreads) void attn_bf16_finalize(Args a, const 
             if constexpr (F32)
                 v[j] = *reinterpret_cast<const f32xE*>(a.part_o + pe);
             else
-                v[j] = __builtin_convertvector(*reinterpret_cast<const bf16xE*>(reinterpret_cast<const __bf16*>(a.part_o) + pe),
-                                               f32xE);
+                v[j] = __builtin_convertvector(
+                    *reinterpret_cast<const bf16xE*>(reinterpret_cast<const __bf16*>(a.part_o) + pe), f32xE);
         }
+    };
+    auto merge = [&](int sg0, const float (&l)[4], const f32xE (&v)[4]) __attribute__((always_inline)) {
         float mg = M;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             if (sg0 + j <= s1) mg = fmaxf(mg, l[j]);
-        if (mg == -INFINITY) continue;
+        if (mg == -INFINITY) return;
         const float sc = __expf(M - mg);  // 0 while M is -inf
         Wsum *= sc;
         acc *= sc;
@@ -966,6 +967,16 @@ __global__ __launch_bounds__(kFinThreads) void attn_bf16_finalize(Args a, const 
             acc += w * v[j];
         }
         M = mg;
+    };
+    float la[4], lb[4];
+    f32xE va[4], vb[4];
+    if (s0 <= s1) load(s0, la, va);
+    for (int sg0 = s0; sg0 <= s1; sg0 += 8) {
+        if (sg0 + 4 <= s1) load(sg0 + 4, lb, vb);
+        merge(sg0, la, va);
+        if (sg0 + 4 > s1) break;
+        if (sg0 + 8 <= s1) load(sg0 + 8, la, va);
+        merge(sg0 + 4, lb, vb);
     }
     const float inv = Wsum > 0.f ? 1.f / Wsum : 0.f;
     const f32xE o = acc * inv;
