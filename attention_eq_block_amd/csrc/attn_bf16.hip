@@ -290,7 +290,7 @@ __device__ __forceinline__ void load_tile(Regs<D>& r, const Cur& c, int page, co
     }
 #pragma unroll
     for (int i = 0; i < C::LPG; ++i)
-        r.x[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + off[i]));
+        r.x[i] = *reinterpret_cast<const u32x4*>(base + off[i]);
 }
 
 // registers -> LDS half tile with row pitch `pitch`
