@@ -47,6 +47,18 @@ class ConfUnmaskParams(ctypes.Structure):
     ]
 
 
+class KvAppendParams(ctypes.Structure):
+    _fields_ = [
+        ("dtype", c_i32), ("B", c_i32), ("S", c_i32), ("Hkv", c_i32), ("head_dim", c_i32),
+        ("Kctx", c_ptr), ("Vctx", c_ptr),
+        ("page_size", c_i32), ("num_pages", c_i32), ("max_pages", c_i32),
+        ("page_table", c_ptr), ("ctx_len", c_ptr),
+        ("Knew", c_ptr), ("Vnew", c_ptr),
+        ("new_stride_b", c_i64), ("new_stride_s", c_i64), ("new_stride_h", c_i64),
+        ("pool", c_ptr), ("pool_count", c_ptr), ("status", c_ptr),
+    ]
+
+
 class TTError(RuntimeError):
     def __init__(self, code: int, what: str):
         self.code = code
@@ -79,6 +91,8 @@ def lib():
         L.tt_conf_unmask_workspace_bytes.argtypes = [ctypes.POINTER(ConfUnmaskParams)]
         L.tt_conf_unmask.restype = ctypes.c_int
         L.tt_conf_unmask.argtypes = [ctypes.POINTER(ConfUnmaskParams), c_ptr, c_size, c_ptr]
+        L.tt_kv_append.restype = ctypes.c_int
+        L.tt_kv_append.argtypes = [ctypes.POINTER(KvAppendParams), c_ptr]
         _lib = L
     return _lib
 

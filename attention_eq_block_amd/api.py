@@ -7,7 +7,8 @@ kernels. torch provides device memory and streams.
 Method: Nemotron-TwoTower (arXiv 2606.26493): ``block_attn`` is Eq. (1) of
 section 2.1, ``lse_merge`` combines partial attentions over disjoint parts of
 Eq. (1)'s key set, ``conf_unmask`` is the ConfidenceSample step of
-Algorithm 2 (section 2.2).
+Algorithm 2 (section 2.2), ``kv_append`` grows a layer's context cache by a
+committed block (Algorithm 1, section 2.1).
 """
 from __future__ import annotations
 
@@ -17,7 +18,7 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import TT_BF16, TT_F32, BlockAttnParams, ConfUnmaskParams, check, lib
+from ._lib import TT_BF16, TT_F32, BlockAttnParams, ConfUnmaskParams, KvAppendParams, check, lib
 
 _DT = {torch.bfloat16: TT_BF16, torch.float32: TT_F32}
 
@@ -203,6 +204,55 @@ def conf_unmask_workspace_bytes(p: ConfUnmaskParams) -> int:
     return int(lib().tt_conf_unmask_workspace_bytes(p))
 
 
+def append_params(Kc, Vc, page_table, ctx_len, Knew, Vnew, *, pool=None, pool_count=None,
+                  status=None) -> KvAppendParams:
+    """Build the parameter struct for ``tt_kv_append`` (allocating ``status`` if absent)."""
+    num_pages, Hkv, page_size, D = Kc.shape
+    B, S = Knew.shape[0], Knew.shape[1]
+    if not (Kc.is_contiguous() and Vc.is_contiguous()) or Vc.shape != Kc.shape or Vc.dtype != Kc.dtype:
+        raise ValueError("the paged caches must be dense and alike [num_pages][Hkv][page_size][head_dim]")
+    if Knew.dtype != Kc.dtype or Vnew.dtype != Kc.dtype:
+        raise TypeError("new rows must have the cache's dtype")
+    if tuple(Knew.shape) != (B, S, Hkv, D) or Knew.stride() != Vnew.stride() or Knew.stride(3) != 1:
+        raise ValueError("Knew and Vnew must be [B][S][Hkv][head_dim] with equal strides, head_dim contiguous")
+    if page_table.dtype != torch.int32 or not page_table.is_contiguous() or page_table.shape[0] != B:
+        raise ValueError("page_table must be dense int32 [B][max_pages]")
+    if ctx_len.dtype != torch.int32 or tuple(ctx_len.shape) != (B,):
+        raise ValueError("ctx_len must be int32 [B]")
+    if (pool is None) != (pool_count is None):
+        raise ValueError("pool and pool_count go together")
+    for t, name in ((pool, "pool"), (pool_count, "pool_count")):
+        if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
+            raise ValueError(f"{name} must be dense int32")
+    if status is None:
+        status = torch.full((1,), -1, dtype=torch.int32, device=Kc.device)
+    p = KvAppendParams()
+    p.dtype = _code(Kc)
+    p.B, p.S, p.Hkv, p.head_dim = B, S, Hkv, D
+    p.Kctx, p.Vctx = _ptr(Kc), _ptr(Vc)
+    p.page_size, p.num_pages, p.max_pages = page_size, num_pages, page_table.shape[1]
+    p.page_table, p.ctx_len = _ptr(page_table), _ptr(ctx_len)
+    p.Knew, p.Vnew = _ptr(Knew), _ptr(Vnew)
+    p.new_stride_b, p.new_stride_s, p.new_stride_h = Knew.stride(0), Knew.stride(1), Knew.stride(2)
+    p.pool, p.pool_count, p.status = _ptr(pool), _ptr(pool_count), _ptr(status)
+    p._keep = (status,)
+    return p
+
+
+def kv_append(Kc, Vc, page_table, ctx_len, Knew, Vnew, *, pool=None, pool_count=None, status=None):
+    """Append each sequence's S new K/V rows at its ctx_len, in place, and grow ctx_len by S.
+
+    Kc, Vc [num_pages][Hkv][page_size][D]; page_table [B][max_pages] int32 (entries < 0 are
+    filled from ``pool``); ctx_len [B] int32; Knew, Vnew [B][S][Hkv][D]; pool int32 page ids with
+    pool_count a one-element int32 tensor. Returns the one-element int32 status tensor (device):
+    0 appended, 1 capacity, 2 pool exhausted, 3 page id out of range (then nothing changed).
+    """
+    _need_cuda(Kc, Vc, page_table, ctx_len, Knew, Vnew, pool, pool_count, status)
+    p = append_params(Kc, Vc, page_table, ctx_len, Knew, Vnew, pool=pool, pool_count=pool_count, status=status)
+    check(lib().tt_kv_append(p, _stream(Kc)), "tt_kv_append")
+    return p._keep[0]
+
+
 def abi_version() -> int:
     return int(lib().tt_abi_version())
 
@@ -211,6 +261,6 @@ def status_string(code: int) -> str:
     return lib().tt_status_string(code).decode()
 
 
-__all__ = ["block_attn", "lse_merge", "conf_unmask", "attn_params", "unmask_params",
+__all__ = ["block_attn", "lse_merge", "conf_unmask", "kv_append", "attn_params", "unmask_params", "append_params",
            "block_attn_workspace_bytes", "conf_unmask_workspace_bytes", "abi_version", "status_string",
            "TT_F32", "TT_BF16", "_lib"]

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtwotower_attn.so")
 
-SOURCES = ["api.cpp", "attn_bf16.hip", "attn_f32.hip", "merge.hip", "unmask.hip"]
+SOURCES = ["api.cpp", "attn_bf16.hip", "attn_f32.hip", "kv_append.hip", "merge.hip", "unmask.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -97,6 +97,26 @@ tt_status validate_unmask(const tt_conf_unmask_params* p) {
     return TT_OK;
 }
 
+tt_status validate_append(const tt_kv_append_params* p) {
+    if (!p) return TT_ERR_NULL;
+    if (p->dtype != TT_BF16 && p->dtype != TT_F32) return TT_ERR_DTYPE;
+    if (p->B < 0 || p->S < 1 || p->S > 64 || p->Hkv < 1 || p->head_dim < 1) return TT_ERR_SHAPE;
+    if (p->page_size < 1 || p->num_pages < 1 || p->max_pages < 1) return TT_ERR_SHAPE;
+    if ((int64_t)p->B * p->max_pages >= ((int64_t)1 << 30)) return TT_ERR_UNSUPPORTED;
+    if (((int64_t)p->head_dim * esize(p->dtype)) % 16 != 0) return TT_ERR_UNSUPPORTED;
+    if (p->B == 0) return TT_OK;
+    if (!p->Kctx || !p->Vctx || !p->page_table || !p->ctx_len || !p->Knew || !p->Vnew || !p->status)
+        return TT_ERR_NULL;
+    if ((p->pool == nullptr) != (p->pool_count == nullptr)) return TT_ERR_NULL;
+    if (!aligned16(p->Kctx) || !aligned16(p->Vctx) || !aligned16(p->Knew) || !aligned16(p->Vnew))
+        return TT_ERR_UNSUPPORTED;
+    if (!stride_ok(p->new_stride_b, p->dtype) || !stride_ok(p->new_stride_s, p->dtype) ||
+        !stride_ok(p->new_stride_h, p->dtype))
+        return TT_ERR_UNSUPPORTED;
+    if ((int64_t)p->B * p->S >= ((int64_t)1 << 31)) return TT_ERR_SHAPE;
+    return TT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -176,6 +196,19 @@ tt_status tt_conf_unmask(const tt_conf_unmask_params* p, void* workspace, size_t
             fprintf(stderr, "[tt] conf_unmask B=%d S=%d V=%d vsplit=%d gamma=%g T=%g R=%d\n", p->B, p->S, p->V,
                     plan.n_vsplit, p->gamma, p->temperature, p->steps_left);
         return tt::launch_unmask(*p, plan, workspace, stream);
+    } catch (...) {
+        return TT_ERR_HIP;
+    }
+}
+
+tt_status tt_kv_append(const tt_kv_append_params* p, hipStream_t stream) {
+    const tt_status v = validate_append(p);
+    if (v != TT_OK || p->B == 0) return v;
+    try {
+        if (log_enabled())
+            fprintf(stderr, "[tt] kv_append B=%d S=%d Hkv=%d d=%d page=%d pages=%d\n", p->B, p->S, p->Hkv,
+                    p->head_dim, p->page_size, p->num_pages);
+        return tt::launch_kv_append(*p, stream);
     } catch (...) {
         return TT_ERR_HIP;
     }

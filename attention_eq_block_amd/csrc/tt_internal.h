@@ -42,6 +42,8 @@ tt_status launch_attn_bf16(const tt_block_attn_params& p, const AttnPlan& plan, 
 
 tt_status launch_attn_f32(const tt_block_attn_params& p, hipStream_t s);
 
+tt_status launch_kv_append(const tt_kv_append_params& p, hipStream_t s);
+
 tt_status launch_lse_merge(int P, const float* O_parts, const float* lse_parts, int B, int S, int Hq,
                            int d, void* O_out, int o_dtype, float* lse_out, hipStream_t s);
 

@@ -217,6 +217,40 @@ def random_mask_state(B: int, S: int, p_masked: float, seed: int = 0, device="cp
 
 
 # ----------------------------------------------------------------------------
+# commit-time cache append
+# ----------------------------------------------------------------------------
+
+SUB_APPEND = 12
+
+
+def make_append_inputs(B: int, S: int, Hkv: int, D: int, page_size: int, max_pages: int, ctx_lens,
+                       spare_pages: int, dtype=torch.bfloat16, seed: int = 0, assign_all: bool = False):
+    """Paged caches and one committed block of new K/V rows per sequence.
+
+    The cache holds the pages each sequence uses for its ctx_lens (every page of
+    max_pages when ``assign_all``) plus ``spare_pages`` free ones, all in one seeded
+    random order; table entries past the used pages are -1 and the free pages form
+    the pool. Cache contents and new rows are N(0,1). CPU tensors; the pool is int32.
+    """
+    ctx = [int(c) for c in ctx_lens]
+    used = [max_pages if assign_all else (max(c, 0) + page_size - 1) // page_size for c in ctx]
+    num_pages = sum(used) + spare_pages
+    perm = torch.randperm(num_pages, generator=_gen(seed, SUB_APPEND)).to(torch.int32)
+    table = torch.full((B, max_pages), -1, dtype=torch.int32)
+    k = 0
+    for b in range(B):
+        table[b, :used[b]] = perm[k:k + used[b]]
+        k += used[b]
+    pool = perm[k:].clone()
+    Kc = randn((num_pages, Hkv, page_size, D), seed, SUB_APPEND + 1, dtype=dtype)
+    Vc = randn((num_pages, Hkv, page_size, D), seed, SUB_APPEND + 2, dtype=dtype)
+    Kn = randn((B, S, Hkv, D), seed, SUB_APPEND + 3, dtype=dtype)
+    Vn = randn((B, S, Hkv, D), seed, SUB_APPEND + 4, dtype=dtype)
+    return dict(Kc=Kc, Vc=Vc, page_table=table, ctx_len=torch.tensor(ctx, dtype=torch.int32), Knew=Kn, Vnew=Vn,
+                pool=pool, pool_count=int(pool.numel()))
+
+
+# ----------------------------------------------------------------------------
 # the five workloads
 # ----------------------------------------------------------------------------
 

@@ -261,6 +261,72 @@ def run_single(args, name):
     return res
 
 
+APPEND_METRIC = "committed-block KV rows appended per s (one layer); achieved HBM GB/s vs peak"
+
+
+def run_append(args):
+    """Commit-time cache append (Algorithm 1's context update) at the denoise loop's shape: the
+    S = 16 committed rows of 32 sequences with prefix 8192, 2 KV heads, d = 128, bf16, 16-token
+    pages, a fresh page taken from the pool per sequence. Each call is timed on its own (HIP events
+    on the stream); the cache state is restored between calls outside the timed region."""
+    B, S, Hkv, D, P = 32, 16, 2, 128, 16
+    L0 = 8192 - 8  # mid-page: every sequence fills its last page and takes one more
+    inp = synth.make_append_inputs(B, S, Hkv, D, P, max_pages=520, ctx_lens=[L0] * B, spare_pages=64, seed=0)
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    table0, ctx0 = d["page_table"].clone(), d["ctx_len"].clone()
+    pc = torch.tensor([inp["pool_count"]], dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    p = api.append_params(d["Kc"], d["Vc"], d["page_table"], d["ctx_len"], d["Knew"], d["Vnew"], pool=d["pool"],
+                          pool_count=pc, status=status)
+    lib = api.lib()
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def reset():
+        d["page_table"].copy_(table0)
+        d["ctx_len"].copy_(ctx0)
+        pc.fill_(inp["pool_count"])
+
+    for _ in range(args.warmup):
+        reset()
+        assert lib.tt_kv_append(p, sh) == 0
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e0, e1 in ev:
+        reset()
+        e0.record(stream)
+        rc = lib.tt_kv_append(p, sh)
+        e1.record(stream)
+        if rc:
+            raise RuntimeError(f"tt_kv_append failed: {api.status_string(rc)}")
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0 and int(d["ctx_len"][0].item()) == L0 + S
+    call_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / len(ev)
+    esz = 2
+    algo = 2 * 2 * B * S * Hkv * D * esz + B * (2 * 4 + 2 * 4)  # rows read and written; ctx_len and table entries
+    achieved = algo / (call_ms * 1e-3) / 1e9
+    res = {"metric": APPEND_METRIC, "value": B * S / (call_ms * 1e-3), "unit": "rows/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": call_ms, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": f"kv append: B={B}, S={S}, {Hkv} kv heads, d={D}, 16-token pages, prefix {L0}",
+                      "global_batch": B, "seq_len": L0 + S, "parallelism": "none", "call_us": call_ms * 1e3},
+           "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": achieved / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes": algo,
+                        "note": "two launches (plan, copy) of under 1 MB: launch latency, not bandwidth"}}
+    if not args.no_cpu:
+        import oracle
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < 2.0:
+            r = oracle.kv_append(inp["Kc"], inp["Vc"], inp["page_table"], inp["ctx_len"], inp["Knew"], inp["Vnew"],
+                                 pool=inp["pool"].tolist(), pool_count=inp["pool_count"])
+            assert r["status"] == 0
+            n += 1
+        dt = (time.perf_counter() - t0) / n
+        res["cpu_baseline"] = {"value": B * S / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
+                               "sample": f"the whole call, {n} runs (each copies the caches first)"}
+    return res
+
+
 def copy_calibration():
     """A plain device-to-device copy of COPY_BYTES, five times: the counter reference
     for FETCH_SIZE / WRITE_SIZE (each launch reads and writes COPY_BYTES)."""
@@ -277,7 +343,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="loop", choices=["loop", "single", "ragged", "long"])
+    ap.add_argument("--workload", default="loop", choices=["loop", "single", "ragged", "long", "append"])
     ap.add_argument("--gamma", type=float, default=0.8)
     ap.add_argument("--temperature", type=float, default=0.1)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -294,7 +360,12 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
-    res = run_loop(args) if args.workload == "loop" else run_single(args, args.workload)
+    if args.workload == "loop":
+        res = run_loop(args)
+    elif args.workload == "append":
+        res = run_append(args)
+    else:
+        res = run_single(args, args.workload)
     print(json.dumps(res))
 
 

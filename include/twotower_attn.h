@@ -14,6 +14,9 @@
  *   - tt_conf_unmask: section 2.2 ("Sampling"), Algorithm 2, the
  *     ConfidenceSample step: commit the masked predictions whose confidence
  *     exceeds gamma, so that the block still completes within the steps left.
+ *   - tt_kv_append: section 2.1, Algorithm 1, the update of the AR context
+ *     after a block is committed: the context cache of each attention layer
+ *     grows by the committed block's keys and values.
  *
  * Conventions shared by every call:
  *   - Pointers named as tensors are DEVICE pointers owned by the caller. The
@@ -212,6 +215,63 @@ size_t tt_conf_unmask_workspace_bytes(const tt_conf_unmask_params* p);
 
 tt_status tt_conf_unmask(const tt_conf_unmask_params* p, void* workspace, size_t ws_bytes,
                          hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * Commit-time KV append: the context cache grows by the committed block
+ * ------------------------------------------------------------------------ *
+ * Algorithm 1 (section 2.1): once block b is committed, the context tower
+ * runs causally over its S tokens and extends its per-layer KV cache, so the
+ * next block's Eq. (1) sees a prefix longer by S. This call is the cache side
+ * of that update for one layer: the S new rows of every sequence b are written
+ * at prefix positions ctx_len[b] .. ctx_len[b]+S-1 and ctx_len[b] grows by S.
+ *
+ * Position j of sequence b is slot j % page_size of page
+ * page_table[b*max_pages + j / page_size] (the layout tt_block_attn reads).
+ * A table entry < 0 that a new position needs is filled from the caller's
+ * pool of free page ids, pool[0 .. *pool_count-1], taken from the top: the
+ * first page needed (lowest sequence, then lowest position) gets
+ * pool[*pool_count-1], the next pool[*pool_count-2], and so on; *pool_count
+ * decreases by the number taken. The assignment is therefore deterministic.
+ *
+ * All or nothing: the call changes no cache row, table entry, ctx_len or
+ * *pool_count, and writes *status != 0, if any sequence would pass
+ * max_pages*page_size positions (status 1), more pages are needed than the
+ * pool holds (status 2; pool may be NULL when no page is needed), or a page id
+ * it would write to (from the table or the pool) is outside [0, num_pages)
+ * (status 3). Otherwise it performs the append and writes *status = 0.
+ * status is device memory; read it after the stream reaches the call.
+ *
+ *   Kctx, Vctx [num_pages][Hkv][page_size][head_dim] of dtype, in/out
+ *   page_table [B][max_pages] int32, in/out
+ *   ctx_len    [B] int32, in/out (a negative length counts as 0)
+ *   Knew, Vnew [B][S][Hkv][head_dim] of dtype at base + b*new_stride_b +
+ *              s*new_stride_s + g*new_stride_h
+ *   pool       int32 page ids (device, may be NULL); pool_count, status: one
+ *              device int32 each
+ * Requires dtype TT_BF16 or TT_F32, B >= 0, 1 <= S <= 64, Hkv >= 1,
+ * head_dim >= 1 with head_dim * element size a multiple of 16 bytes,
+ * page_size >= 1, num_pages >= 1, max_pages >= 1, B*max_pages below 2^30;
+ * Kctx, Vctx, Knew, Vnew 16-byte aligned with strides that keep 16-byte
+ * alignment (TT_ERR_UNSUPPORTED otherwise). The new rows must not overlap the
+ * cache. Needs no workspace.
+ */
+typedef struct tt_kv_append_params {
+    int32_t dtype;  /* tt_dtype of the caches and the new rows */
+    int32_t B, S, Hkv, head_dim;
+    void* Kctx;
+    void* Vctx;
+    int32_t page_size, num_pages, max_pages;
+    int32_t* page_table;
+    int32_t* ctx_len;
+    const void* Knew;
+    const void* Vnew;
+    int64_t new_stride_b, new_stride_s, new_stride_h;
+    const int32_t* pool;
+    int32_t* pool_count;
+    int32_t* status;
+} tt_kv_append_params;
+
+tt_status tt_kv_append(const tt_kv_append_params* p, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -7,7 +7,9 @@ HIP library and never calls it.
 Each function follows the Nemotron-TwoTower paper (arXiv 2606.26493):
 ``block_attn`` is Eq. (1) of section 2.1, ``lse_merge`` is the split of
 Eq. (1)'s concatenated key set into disjoint parts, ``conf_unmask`` is the
-ConfidenceSample step of Algorithm 2 (section 2.2, "Sampling").
+ConfidenceSample step of Algorithm 2 (section 2.2, "Sampling"),
+``kv_append`` is the cache side of Algorithm 1's context update after a
+block is committed (section 2.1).
 """
 from __future__ import annotations
 
@@ -49,6 +51,8 @@ def _bind(lib):
     lib.oracle_conf_unmask.argtypes = [_I, _I, _I, _I, ctypes.c_longlong, _P, _P, _P, ctypes.c_double,
                                        ctypes.c_double, _I, _P, _P, _P, _P, _P]
     lib.oracle_num_threads.restype = _I
+    lib.oracle_kv_append.restype = _I
+    lib.oracle_kv_append.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P]
     return lib
 
 
@@ -177,6 +181,39 @@ def conf_unmask(logits, mask, tokens, *, gamma: float, temperature: float, steps
         raise ValueError("oracle_conf_unmask rejected its arguments")
     del la
     return dict(tokens=tok_out, mask=mask_out, conf=conf, argmax=am, num_masked=nm)
+
+
+def kv_append(Kc, Vc, page_table, ctx_len, Knew, Vnew, pool=None, pool_count=0):
+    """Commit-time cache append (Algorithm 1, section 2.1) on CPU copies; inputs are unchanged.
+
+    Kc, Vc [num_pages][Hkv][page_size][D] (float32 or bfloat16); page_table [B][max_pages];
+    ctx_len [B]; Knew, Vnew [B][S][Hkv][D] of the cache's dtype; pool: page ids (or None) with
+    pool_count of them in use. Returns dict(Kc, Vc, page_table, ctx_len, pool_count, status) with
+    torch tensors for the caches and numpy arrays for the integers.
+    """
+    num_pages, Hkv, page_size, D = Kc.shape
+    B, S = Knew.shape[0], Knew.shape[1]
+    dt = Kc.dtype
+    if Vc.dtype != dt or Knew.dtype != dt or Vnew.dtype != dt:
+        raise TypeError("caches and new rows must share a dtype")
+    esz = {torch.float32: 4, torch.bfloat16: 2}[dt]
+
+    def raw(t):
+        t = t.detach().to("cpu").contiguous().clone()
+        return t, t.view(torch.uint8).numpy()
+
+    Kt, ka = raw(Kc)
+    Vt, va = raw(Vc)
+    _, kn = raw(Knew)
+    _, vn = raw(Vnew)
+    pt = _i32(page_table).reshape(B, -1).copy()
+    cl = _i32(ctx_len).copy()
+    pl = _i32(pool if pool is not None else [0]).copy()
+    pc = np.array([int(pool_count)], np.int32)
+    rc = load().oracle_kv_append(esz, B, S, Hkv, D, page_size, num_pages, pt.shape[1], ka.ctypes.data,
+                                 va.ctypes.data, pt.ctypes.data, cl.ctypes.data, kn.ctypes.data, vn.ctypes.data,
+                                 pl.ctypes.data, pc.ctypes.data if pool is not None else None)
+    return dict(Kc=Kt, Vc=Vt, page_table=pt, ctx_len=cl, pool_count=int(pc[0]), status=int(rc))
 
 
 def f32(x: float) -> float:

@@ -9,7 +9,8 @@
  *
  * Source: "Nemotron-TwoTower: Diffusion Language Modeling with Pretrained
  * Autoregressive Context" (arXiv 2606.26493), section 2.1 "Bidirectional
- * attention", Eq. (1), and section 2.2 "Sampling", Algorithm 2.
+ * attention", Eq. (1), and section 2.2 "Sampling", Algorithm 2; the
+ * commit-time cache append follows Algorithm 1 of section 2.1.
  *
  * Every function is the plain definition, written out in double precision
  * over the exactly decoded inputs (a bf16 value widened to double is exact).
@@ -236,5 +237,69 @@ int oracle_conf_unmask(int dtype, int B, int S, int V, long long row_stride, con
         }
         num_masked_out[b] = M - committed;
     }
+    return 0;
+}
+
+/* Commit-time KV append (Algorithm 1, section 2.1: after block b is committed
+ * the context tower extends its KV cache, so the next block sees a prefix
+ * longer by S). For every sequence b with L = max(ctx_len[b], 0), new row s
+ * goes to prefix position L + s, which is slot (L + s) % page_size of page
+ * page_table[b][(L + s) / page_size], and ctx_len[b] becomes L + S. A table
+ * entry below 0 that a new position needs takes a page from the top of the
+ * pool, in the order sequence first, then position. Elements are copied as
+ * raw bytes (esz bytes each); Kn and Vn are dense [B][S][Hkv][D].
+ * All or nothing: returns 1 if a sequence would pass max_pages * page_size
+ * positions, 2 if the pool holds too few pages, 3 if a page id it would write
+ * to is outside [0, num_pages), and then changes nothing; else 0. */
+int oracle_kv_append(int esz, int B, int S, int Hkv, int D, int page_size, int num_pages, int max_pages,
+                     unsigned char* Kc, unsigned char* Vc, int* page_table, int* ctx_len,
+                     const unsigned char* Kn, const unsigned char* Vn, const int* pool, int* pool_count) {
+    const long long cap = (long long)max_pages * page_size;
+    for (int b = 0; b < B; ++b) {
+        const int L = ctx_len[b] < 0 ? 0 : ctx_len[b];
+        if ((long long)L + S > cap) return 1;
+    }
+    int needed = 0, bad = 0;
+    for (int b = 0; b < B; ++b) {
+        const int L = ctx_len[b] < 0 ? 0 : ctx_len[b];
+        for (int p = L / page_size; p <= (L + S - 1) / page_size; ++p) {
+            const int e = page_table[(size_t)b * max_pages + p];
+            if (e < 0) ++needed;
+            else if (e >= num_pages) bad = 1;
+        }
+    }
+    const int count = pool_count && *pool_count > 0 ? *pool_count : 0;
+    if (needed > count) return 2;
+    for (int k = 0; k < needed; ++k) {
+        const int pg = pool[count - 1 - k];
+        if (pg < 0 || pg >= num_pages) bad = 1;
+    }
+    if (bad) return 3;
+    int k = 0;
+    for (int b = 0; b < B; ++b) {
+        const int L = ctx_len[b] < 0 ? 0 : ctx_len[b];
+        for (int p = L / page_size; p <= (L + S - 1) / page_size; ++p) {
+            int* e = &page_table[(size_t)b * max_pages + p];
+            if (*e < 0) *e = pool[count - 1 - k++];
+        }
+    }
+    const size_t row = (size_t)D * esz;
+    for (int b = 0; b < B; ++b) {
+        const int L = ctx_len[b] < 0 ? 0 : ctx_len[b];
+        for (int s = 0; s < S; ++s) {
+            const int j = L + s;
+            const int pidx = j / page_size;
+            const int page = page_table[(size_t)b * max_pages + pidx];
+            const int slot = j % page_size;
+            for (int g = 0; g < Hkv; ++g) {
+                const size_t dst = (((size_t)page * Hkv + g) * page_size + slot) * row;
+                const size_t src = (((size_t)b * S + s) * Hkv + g) * row;
+                memcpy(Kc + dst, Kn + src, row);
+                memcpy(Vc + dst, Vn + src, row);
+            }
+        }
+        ctx_len[b] = L + S;
+    }
+    if (needed > 0) *pool_count = count - needed;
     return 0;
 }

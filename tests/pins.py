@@ -503,4 +503,174 @@ def pin_unmask_bf16_widening():
     close(a["conf"], b["conf"], 0.0, "bf16 vs widened conf")
 
 
+# ----------------------------------------------------------------------------
+# commit-time cache append (Algorithm 1, section 2.1)
+# ----------------------------------------------------------------------------
+
+def _append_case(B=5, S=5, Hkv=2, D=4, page_size=4, max_pages=6, ctx=(0, 3, 8, 13, -2), spare=12, seed=0,
+                 dtype=torch.float32, unassign_tail=True):
+    """Random caches whose pages are a shuffled pool; entries past each sequence's used pages are -1
+    (when unassign_tail) and the spare pages form the pool."""
+    g = torch.Generator().manual_seed(seed)
+    used = [max(0, (max(c, 0) + page_size - 1) // page_size) for c in ctx]
+    full = [max_pages] * B
+    n_assigned = sum(used) if unassign_tail else sum(full)
+    num_pages = n_assigned + spare
+    perm = torch.randperm(num_pages, generator=g).tolist()
+    table = torch.full((B, max_pages), -1, dtype=torch.int32)
+    k = 0
+    for b in range(B):
+        for p in range(used[b] if unassign_tail else max_pages):
+            table[b, p] = perm[k]
+            k += 1
+    pool = perm[k:]
+    Kc = torch.randn(num_pages, Hkv, page_size, D, generator=g).to(dtype)
+    Vc = torch.randn(num_pages, Hkv, page_size, D, generator=g).to(dtype)
+    Kn = torch.randn(B, S, Hkv, D, generator=g).to(dtype)
+    Vn = torch.randn(B, S, Hkv, D, generator=g).to(dtype)
+    return dict(Kc=Kc, Vc=Vc, page_table=table, ctx_len=torch.tensor(ctx, dtype=torch.int32), Knew=Kn, Vnew=Vn,
+                pool=pool, pool_count=len(pool))
+
+
+def _run_append(c):
+    return oracle.kv_append(c["Kc"], c["Vc"], c["page_table"], c["ctx_len"], c["Knew"], c["Vnew"],
+                            pool=c["pool"], pool_count=c["pool_count"])
+
+
+def pin_append_gather():
+    """After the append, each sequence's prefix read page by page is its old prefix followed by the
+    new rows; ctx_len grows by S; the slots of no sequence's new positions keep their values."""
+    for dtype in (torch.float32, torch.bfloat16):
+        c = _append_case(dtype=dtype)
+        r = _run_append(c)
+        assert r["status"] == 0
+        S = c["Knew"].shape[1]
+        L0 = [max(int(x), 0) for x in c["ctx_len"]]
+        assert r["ctx_len"].tolist() == [l + S for l in L0]
+        touched = set()
+        for b in range(len(L0)):
+            before = gather_prefix(c["Kc"], c["page_table"], torch.tensor(L0), b)
+            after_k = gather_prefix(r["Kc"], torch.from_numpy(r["page_table"]), torch.from_numpy(r["ctx_len"]), b)
+            after_v = gather_prefix(r["Vc"], torch.from_numpy(r["page_table"]), torch.from_numpy(r["ctx_len"]), b)
+            want_k = torch.cat([before, c["Knew"][b].transpose(0, 1)], dim=1)
+            before_v = gather_prefix(c["Vc"], c["page_table"], torch.tensor(L0), b)
+            want_v = torch.cat([before_v, c["Vnew"][b].transpose(0, 1)], dim=1)
+            assert torch.equal(after_k, want_k), f"K of sequence {b}"
+            assert torch.equal(after_v, want_v), f"V of sequence {b}"
+            P = c["Kc"].shape[2]
+            for j in range(L0[b], L0[b] + S):
+                touched.add((int(r["page_table"][b, j // P]), j % P))
+        for pg in range(c["Kc"].shape[0]):
+            for sl in range(c["Kc"].shape[2]):
+                if (pg, sl) not in touched:
+                    assert torch.equal(r["Kc"][pg, :, sl], c["Kc"][pg, :, sl]), "an untouched K slot changed"
+                    assert torch.equal(r["Vc"][pg, :, sl], c["Vc"][pg, :, sl]), "an untouched V slot changed"
+
+
+def pin_append_contiguous_slice():
+    """With one run of pages per sequence (identity table), the append is a slice assignment on the
+    [B][Hkv][max_pages*page_size][D] view of the cache."""
+    B, S, Hkv, D, P, mp = 3, 6, 2, 4, 4, 5
+    g = torch.Generator().manual_seed(3)
+    Kc = torch.randn(B * mp, Hkv, P, D, generator=g)
+    Vc = torch.randn(B * mp, Hkv, P, D, generator=g)
+    table = torch.arange(B * mp, dtype=torch.int32).reshape(B, mp)
+    ctx = torch.tensor([0, 7, 14], dtype=torch.int32)
+    Kn = torch.randn(B, S, Hkv, D, generator=g)
+    Vn = torch.randn(B, S, Hkv, D, generator=g)
+    r = oracle.kv_append(Kc, Vc, table, ctx, Kn, Vn)
+    assert r["status"] == 0
+    for cache, new, out in ((Kc, Kn, r["Kc"]), (Vc, Vn, r["Vc"])):
+        view = cache.reshape(B, mp, Hkv, P, D).permute(0, 2, 1, 3, 4).reshape(B, Hkv, mp * P, D).clone()
+        for b in range(B):
+            L = int(ctx[b])
+            view[b, :, L:L + S] = new[b].transpose(0, 1)
+        got = out.reshape(B, mp, Hkv, P, D).permute(0, 2, 1, 3, 4).reshape(B, Hkv, mp * P, D)
+        assert torch.equal(got, view)
+
+
+def pin_append_pool_order():
+    """Pages come off the top of the pool, sequence by sequence and position by position, and the
+    pool shrinks by exactly that many."""
+    c = _append_case(seed=5)
+    r = _run_append(c)
+    assert r["status"] == 0
+    P = c["Kc"].shape[2]
+    S = c["Knew"].shape[1]
+    order = []
+    for b, L in enumerate(max(int(x), 0) for x in c["ctx_len"]):
+        for p in range(L // P, (L + S - 1) // P + 1):
+            if int(c["page_table"][b, p]) < 0:
+                order.append((b, p))
+    pool = c["pool"]
+    for k, (b, p) in enumerate(order):
+        assert int(r["page_table"][b, p]) == pool[len(pool) - 1 - k], (b, p)
+    assert r["pool_count"] == len(pool) - len(order)
+    keep = r["page_table"] == c["page_table"].numpy()
+    for b, p in order:
+        keep[b, p] = True
+    assert keep.all(), "an entry that needed no page changed"
+
+
+def pin_append_all_or_nothing():
+    """A sequence past capacity (1), a short pool (2) or a page id outside the cache (3) leaves every
+    output as it was; filling exactly to capacity succeeds."""
+    base = _append_case(seed=7)
+    mp, P, S = base["page_table"].shape[1], base["Kc"].shape[2], base["Knew"].shape[1]
+    cases = []
+    c = dict(base); c["ctx_len"] = base["ctx_len"].clone(); c["ctx_len"][1] = mp * P - S + 1
+    cases.append((c, 1))
+    c = dict(base); c["pool_count"] = 7
+    cases.append((c, 2))
+    c = dict(base); c["page_table"] = base["page_table"].clone(); c["page_table"][1, 0] = base["Kc"].shape[0]
+    cases.append((c, 3))
+    c = dict(base); c["pool"] = list(base["pool"]); c["pool"][-1] = -5
+    cases.append((c, 3))
+    for c, code in cases:
+        r = _run_append(c)
+        assert r["status"] == code, (code, r["status"])
+        assert torch.equal(r["Kc"], c["Kc"]) and torch.equal(r["Vc"], c["Vc"])
+        assert np.array_equal(r["page_table"], c["page_table"].numpy())
+        assert np.array_equal(r["ctx_len"], c["ctx_len"].numpy())
+        assert r["pool_count"] == c["pool_count"]
+    c = dict(base); c["ctx_len"] = base["ctx_len"].clone(); c["ctx_len"][1] = mp * P - S
+    r = _run_append(c)
+    assert r["status"] == 0 and int(r["ctx_len"][1]) == mp * P
+
+
+def pin_append_split():
+    """Appending S1 rows and then S2 rows equals appending the S1+S2 rows at once."""
+    c = _append_case(S=7, seed=9)
+    one = _run_append(c)
+    a = dict(c); a["Knew"], a["Vnew"] = c["Knew"][:, :3], c["Vnew"][:, :3]
+    r1 = _run_append(a)
+    b = dict(Kc=r1["Kc"], Vc=r1["Vc"], page_table=torch.from_numpy(r1["page_table"]),
+             ctx_len=torch.from_numpy(r1["ctx_len"]), Knew=c["Knew"][:, 3:], Vnew=c["Vnew"][:, 3:],
+             pool=c["pool"], pool_count=r1["pool_count"])
+    r2 = _run_append(b)
+    assert one["status"] == r1["status"] == r2["status"] == 0
+    assert np.array_equal(one["ctx_len"], r2["ctx_len"])
+    for b_ in range(c["Knew"].shape[0]):
+        k1 = gather_prefix(one["Kc"], torch.from_numpy(one["page_table"]), torch.from_numpy(one["ctx_len"]), b_)
+        k2 = gather_prefix(r2["Kc"], torch.from_numpy(r2["page_table"]), torch.from_numpy(r2["ctx_len"]), b_)
+        assert torch.equal(k1, k2)
+
+
+def pin_append_golden():
+    """Hand-worked appends (tests/golden/hand_cases.json, append)."""
+    for c in json.load(open(GOLDEN))["append"]:
+        P, npg, Hkv, D = c["page_size"], c["num_pages"], c["Hkv"], c["D"]
+        Kc = torch.zeros(npg, Hkv, P, D)
+        Kn = torch.tensor(c["Knew"], dtype=torch.float32)
+        r = oracle.kv_append(Kc, Kc.clone(), torch.tensor(c["page_table"], dtype=torch.int32),
+                             torch.tensor(c["ctx_len"], dtype=torch.int32), Kn, -Kn, pool=c["pool"],
+                             pool_count=c["pool_count"])
+        assert r["status"] == c["expect_status"], c["name"]
+        assert r["page_table"].tolist() == c["expect_page_table"], c["name"]
+        assert r["ctx_len"].tolist() == c["expect_ctx_len"], c["name"]
+        assert r["pool_count"] == c["expect_pool_count"], c["name"]
+        assert r["Kc"].tolist() == c["expect_K_pages"], c["name"]
+        assert torch.equal(r["Vc"], -r["Kc"]), c["name"]
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

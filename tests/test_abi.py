@@ -11,7 +11,7 @@ import subprocess
 import pytest
 
 from attention_eq_block_amd import _lib
-from attention_eq_block_amd._lib import TT_BF16, TT_F32, BlockAttnParams, ConfUnmaskParams
+from attention_eq_block_amd._lib import TT_BF16, TT_F32, BlockAttnParams, ConfUnmaskParams, KvAppendParams
 
 FAKE = 0x1000  # never dereferenced: every call below must fail validation first
 
@@ -24,7 +24,7 @@ def test_library_loads_and_reports_version():
 def test_exports_every_header_function():
     names = _lib.header_functions()
     assert set(names) == {"tt_abi_version", "tt_status_string", "tt_block_attn", "tt_block_attn_workspace_bytes",
-                          "tt_lse_merge", "tt_conf_unmask", "tt_conf_unmask_workspace_bytes"}
+                          "tt_lse_merge", "tt_conf_unmask", "tt_conf_unmask_workspace_bytes", "tt_kv_append"}
     L = _lib.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -159,3 +159,34 @@ def test_unmask_gamma_extremes_are_valid_arguments():
 def test_merge_validation(args, code):
     rc = _lib.lib().tt_lse_merge(*args, None)
     assert rc == code
+
+
+def append_ok(**kw):
+    p = KvAppendParams()
+    p.dtype, p.B, p.S, p.Hkv, p.head_dim = TT_BF16, 4, 16, 2, 128
+    p.Kctx = p.Vctx = p.page_table = p.ctx_len = p.Knew = p.Vnew = p.status = FAKE
+    p.page_size, p.num_pages, p.max_pages = 16, 64, 16
+    p.new_stride_b, p.new_stride_s, p.new_stride_h = 16 * 2 * 128, 2 * 128, 128
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), 3), (dict(B=-1), 2), (dict(S=0), 2), (dict(S=65), 2), (dict(Hkv=0), 2), (dict(head_dim=0), 2),
+    (dict(page_size=0), 2), (dict(num_pages=0), 2), (dict(max_pages=0), 2), (dict(head_dim=4), 4),
+    (dict(dtype=TT_F32, head_dim=2), 4), (dict(B=1 << 20, max_pages=1 << 10), 4),
+    (dict(Kctx=None), 1), (dict(Vctx=None), 1), (dict(page_table=None), 1), (dict(ctx_len=None), 1),
+    (dict(Knew=None), 1), (dict(Vnew=None), 1), (dict(status=None), 1), (dict(pool=FAKE), 1),
+    (dict(pool_count=FAKE), 1), (dict(Knew=FAKE + 8), 4), (dict(Kctx=FAKE + 2), 4), (dict(new_stride_s=100), 4),
+    (dict(new_stride_h=-8), 4),
+])
+def test_append_validation(kw, code):
+    rc = _lib.lib().tt_kv_append(ctypes.byref(append_ok(**kw)), None)
+    assert rc == code, (kw, _lib.STATUS.get(rc))
+
+
+def test_append_zero_batch_is_a_noop():
+    L = _lib.lib()
+    assert L.tt_kv_append(ctypes.byref(append_ok(B=0, Kctx=None, Knew=None, status=None)), None) == 0
+    assert L.tt_kv_append(None, None) == 1

@@ -47,6 +47,14 @@ MUTANTS = [
     ("fallback ascending", "while (j >= 0 && (cf[ord[j]] < cf[cur]", "while (j >= 0 && (cf[ord[j]] > cf[cur]"),
     ("num_masked not updated", "num_masked_out[b] = M - committed;", "num_masked_out[b] = M;"),
     ("fallback commits one", "for (int i = 0; i < k_min; ++i) {", "for (int i = 0; i < 1 && i < k_min; ++i) {"),
+    ("append slot off by one", "const int slot = j % page_size;", "const int slot = (j + 1) % page_size;"),
+    ("append pool from the bottom", "if (*e < 0) *e = pool[count - 1 - k++];", "if (*e < 0) *e = pool[k++];"),
+    ("append ctx_len not grown", "ctx_len[b] = L + S;", "ctx_len[b] = L;"),
+    ("append capacity off by one", "if ((long long)L + S > cap) return 1;", "if ((long long)L + S >= cap) return 1;"),
+    ("append V from K", "memcpy(Vc + dst, Vn + src, row);", "memcpy(Vc + dst, Kn + src, row);"),
+    ("append pool count kept", "if (needed > 0) *pool_count = count - needed;", ""),
+    ("append new-row index transposed", "const size_t src = (((size_t)b * S + s) * Hkv + g) * row;",
+     "const size_t src = (((size_t)s * B + b) * Hkv + g) * row;"),
 ]
 
 
