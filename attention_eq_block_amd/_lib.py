@@ -59,6 +59,15 @@ class KvAppendParams(ctypes.Structure):
     ]
 
 
+class MaskedNllParams(ctypes.Structure):
+    _fields_ = [
+        ("dtype", c_i32), ("B", c_i32), ("S", c_i32), ("V", c_i32),
+        ("logits", c_ptr), ("logits_stride_row", c_i64),
+        ("targets", c_ptr), ("mask", c_ptr),
+        ("nll", c_ptr), ("loss", c_ptr), ("count", c_ptr),
+    ]
+
+
 class TTError(RuntimeError):
     def __init__(self, code: int, what: str):
         self.code = code
@@ -93,6 +102,10 @@ def lib():
         L.tt_conf_unmask.argtypes = [ctypes.POINTER(ConfUnmaskParams), c_ptr, c_size, c_ptr]
         L.tt_kv_append.restype = ctypes.c_int
         L.tt_kv_append.argtypes = [ctypes.POINTER(KvAppendParams), c_ptr]
+        L.tt_masked_nll_workspace_bytes.restype = c_size
+        L.tt_masked_nll_workspace_bytes.argtypes = [ctypes.POINTER(MaskedNllParams)]
+        L.tt_masked_nll.restype = ctypes.c_int
+        L.tt_masked_nll.argtypes = [ctypes.POINTER(MaskedNllParams), c_ptr, c_size, c_ptr]
         _lib = L
     return _lib
 

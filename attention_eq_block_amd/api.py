@@ -8,7 +8,8 @@ Method: Nemotron-TwoTower (arXiv 2606.26493): ``block_attn`` is Eq. (1) of
 section 2.1, ``lse_merge`` combines partial attentions over disjoint parts of
 Eq. (1)'s key set, ``conf_unmask`` is the ConfidenceSample step of
 Algorithm 2 (section 2.2), ``kv_append`` grows a layer's context cache by a
-committed block (Algorithm 1, section 2.1).
+committed block (Algorithm 1, section 2.1), ``masked_nll`` is the training
+loss L_MD of Eq. (4).
 """
 from __future__ import annotations
 
@@ -18,7 +19,7 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import TT_BF16, TT_F32, BlockAttnParams, ConfUnmaskParams, KvAppendParams, check, lib
+from ._lib import TT_BF16, TT_F32, BlockAttnParams, ConfUnmaskParams, KvAppendParams, MaskedNllParams, check, lib
 
 _DT = {torch.bfloat16: TT_BF16, torch.float32: TT_F32}
 
@@ -253,6 +254,39 @@ def kv_append(Kc, Vc, page_table, ctx_len, Knew, Vnew, *, pool=None, pool_count=
     return p._keep[0]
 
 
+def nll_params(logits, targets, mask, *, nll=None, loss=None, count=None) -> MaskedNllParams:
+    B, S, V = logits.shape
+    if logits.stride(2) != 1 or logits.stride(0) != S * logits.stride(1):
+        raise ValueError("logits rows must be evenly strided with the vocabulary contiguous")
+    for t, name, dt in ((targets, "targets", torch.int32), (mask, "mask", torch.uint8)):
+        if t.dtype != dt or not t.is_contiguous() or tuple(t.shape) != (B, S):
+            raise ValueError(f"{name} must be dense {dt} [B][S]")
+    if nll is not None and (nll.dtype != torch.float32 or not nll.is_contiguous() or tuple(nll.shape) != (B, S)):
+        raise ValueError("nll must be dense float32 [B][S]")
+    if loss is None:
+        loss = torch.zeros(1, dtype=torch.float32, device=logits.device)
+    p = MaskedNllParams()
+    p.dtype = _code(logits)
+    p.B, p.S, p.V = B, S, V
+    p.logits, p.logits_stride_row = _ptr(logits), logits.stride(1)
+    p.targets, p.mask = _ptr(targets), _ptr(mask)
+    p.nll, p.loss, p.count = _ptr(nll), _ptr(loss), _ptr(count)
+    p._keep = (loss,)
+    return p
+
+
+def masked_nll(logits, targets, mask, *, nll=None, count=None, loss=None, workspace=None):
+    """L_MD of Eq. (4): mean over masked positions of logsumexp(x) - x[target]. Returns the loss as a
+    one-element float32 device tensor; ``nll`` [B][S] float32 receives the per-position values and
+    ``count`` (one int32) the number of masked positions, when given."""
+    _need_cuda(logits, targets, mask, nll, count, loss, workspace)
+    p = nll_params(logits, targets, mask, nll=nll, loss=loss, count=count)
+    ws = _ws(int(lib().tt_masked_nll_workspace_bytes(p)), logits.device, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    check(lib().tt_masked_nll(p, _ptr(ws), nbytes, _stream(logits)), "tt_masked_nll")
+    return p._keep[0]
+
+
 def abi_version() -> int:
     return int(lib().tt_abi_version())
 
@@ -261,6 +295,7 @@ def status_string(code: int) -> str:
     return lib().tt_status_string(code).decode()
 
 
-__all__ = ["block_attn", "lse_merge", "conf_unmask", "kv_append", "attn_params", "unmask_params", "append_params",
+__all__ = ["block_attn", "lse_merge", "conf_unmask", "kv_append", "masked_nll", "attn_params", "unmask_params",
+           "append_params", "nll_params",
            "block_attn_workspace_bytes", "conf_unmask_workspace_bytes", "abi_version", "status_string",
            "TT_F32", "TT_BF16", "_lib"]

@@ -97,6 +97,17 @@ tt_status validate_unmask(const tt_conf_unmask_params* p) {
     return TT_OK;
 }
 
+tt_status validate_nll(const tt_masked_nll_params* p) {
+    if (!p) return TT_ERR_NULL;
+    if (p->dtype != TT_BF16 && p->dtype != TT_F32) return TT_ERR_DTYPE;
+    if (p->B < 0 || p->S < 1 || p->V < 1 || p->logits_stride_row < p->V) return TT_ERR_SHAPE;
+    if ((int64_t)p->B * p->S >= (int64_t)1 << 31) return TT_ERR_SHAPE;
+    if (p->B == 0) return TT_OK;
+    if (!p->logits || !p->targets || !p->mask || !p->loss) return TT_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(p->logits) % esize(p->dtype)) != 0) return TT_ERR_UNSUPPORTED;
+    return TT_OK;
+}
+
 tt_status validate_append(const tt_kv_append_params* p) {
     if (!p) return TT_ERR_NULL;
     if (p->dtype != TT_BF16 && p->dtype != TT_F32) return TT_ERR_DTYPE;
@@ -209,6 +220,26 @@ tt_status tt_kv_append(const tt_kv_append_params* p, hipStream_t stream) {
             fprintf(stderr, "[tt] kv_append B=%d S=%d Hkv=%d d=%d page=%d pages=%d\n", p->B, p->S, p->Hkv,
                     p->head_dim, p->page_size, p->num_pages);
         return tt::launch_kv_append(*p, stream);
+    } catch (...) {
+        return TT_ERR_HIP;
+    }
+}
+
+size_t tt_masked_nll_workspace_bytes(const tt_masked_nll_params* p) {
+    if (validate_nll(p) != TT_OK || p->B == 0) return 0;
+    return tt::plan_nll(*p, device_cu_count()).ws_total;
+}
+
+tt_status tt_masked_nll(const tt_masked_nll_params* p, void* workspace, size_t ws_bytes, hipStream_t stream) {
+    const tt_status v = validate_nll(p);
+    if (v != TT_OK || p->B == 0) return v;
+    try {
+        const tt::UnmaskPlan plan = tt::plan_nll(*p, device_cu_count());
+        if (ws_bytes < plan.ws_total || workspace == nullptr) return TT_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return TT_ERR_UNSUPPORTED;
+        if (log_enabled())
+            fprintf(stderr, "[tt] masked_nll B=%d S=%d V=%d vsplit=%d\n", p->B, p->S, p->V, plan.n_vsplit);
+        return tt::launch_nll(*p, plan, workspace, stream);
     } catch (...) {
         return TT_ERR_HIP;
     }

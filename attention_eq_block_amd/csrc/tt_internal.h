@@ -52,8 +52,10 @@ struct UnmaskPlan {
     size_t ws_total;
 };
 UnmaskPlan plan_unmask(const tt_conf_unmask_params& p, int n_cu);
+UnmaskPlan plan_nll(const tt_masked_nll_params& p, int n_cu);
 tt_status launch_unmask(const tt_conf_unmask_params& p, const UnmaskPlan& plan, void* ws,
                         hipStream_t s);
+tt_status launch_nll(const tt_masked_nll_params& p, const UnmaskPlan& plan, void* ws, hipStream_t s);
 
 // prefix length of sequence b as the kernels read it
 __device__ __forceinline__ int clamp_len(int L, int Lmax) { return L < 0 ? 0 : (L > Lmax ? Lmax : L); }

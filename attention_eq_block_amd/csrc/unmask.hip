@@ -10,6 +10,9 @@
 // position: confidence = 1/sum, then the commit rule -- every position above
 // gamma if there are at least ceil(M/steps_left) of them, else the
 // ceil(M/steps_left) most confident (ties to the lower position).
+// The masked-diffusion loss L_MD (Eq. (4)) runs vocab_reduce at temperature 1
+// and a one-workgroup finish (nll_finish): lse - x[target] per masked row and
+// their mean.
 #include <limits.h>
 
 #include "tt_internal.h"
@@ -221,6 +224,51 @@ __global__ __launch_bounds__(64) void unmask_select(UArgs a) {
     if (l == 0 && a.num_masked) a.num_masked[b] = M - ncommit;
 }
 
+// L_MD (section 2.2, Eq. (4)) from the (max, argmax, sum) triples of
+// vocab_reduce at temperature 1: one workgroup, a thread per row, in row
+// order; the loss sums in double, so it does not depend on the launch.
+template <bool BF16>
+__global__ __launch_bounds__(256) void nll_finish(UArgs a, const int* __restrict__ targets, float* nll, float* loss,
+                                                  int* count) {
+    const long long rows = (long long)a.B * a.S;
+    double sum = 0.0;
+    int n = 0;
+    for (long long row = threadIdx.x; row < rows; row += blockDim.x) {
+        if (!a.mask_in[row]) continue;
+        float m = -INFINITY, z = 0.f;
+        int am = INT_MAX;
+        for (int k = 0; k < a.n_vsplit; ++k) {
+            const Triple t = a.part[(long long)k * rows + row];
+            combine(m, am, z, t.m, t.a, t.z, a.c);
+        }
+        const int y = targets[row];
+        float v = __builtin_nanf("");
+        if (y >= 0 && y < a.V) {
+            const char* rp = static_cast<const char*>(a.logits) + row * a.stride * (BF16 ? 2 : 4);
+            v = m + __logf(z) - elem<BF16>(rp, y);
+        }
+        if (nll) nll[row] = v;
+        sum += (double)v;
+        ++n;
+    }
+    __shared__ double ss[256];
+    __shared__ int sn[256];
+    ss[threadIdx.x] = sum;
+    sn[threadIdx.x] = n;
+    __syncthreads();
+    for (int off = 128; off > 0; off >>= 1) {
+        if ((int)threadIdx.x < off) {
+            ss[threadIdx.x] += ss[threadIdx.x + off];
+            sn[threadIdx.x] += sn[threadIdx.x + off];
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        *loss = sn[0] > 0 ? (float)(ss[0] / sn[0]) : 0.f;
+        if (count) *count = sn[0];
+    }
+}
+
 }  // namespace
 
 UnmaskPlan plan_unmask(const tt_conf_unmask_params& p, int n_cu) {
@@ -259,6 +307,34 @@ tt_status launch_unmask(const tt_conf_unmask_params& p, const UnmaskPlan& pl, vo
     else
         hipLaunchKernelGGL(vocab_reduce<false>, grid, dim3(256), 0, s, a);
     hipLaunchKernelGGL(unmask_select, dim3(p.B), dim3(64), 0, s, a);
+    return hipGetLastError() == hipSuccess ? TT_OK : TT_ERR_HIP;
+}
+
+UnmaskPlan plan_nll(const tt_masked_nll_params& p, int n_cu) {
+    tt_conf_unmask_params u{};
+    u.B = p.B;
+    u.S = p.S;
+    u.V = p.V;
+    return plan_unmask(u, n_cu);
+}
+
+tt_status launch_nll(const tt_masked_nll_params& p, const UnmaskPlan& pl, void* ws, hipStream_t s) {
+    UArgs a{};
+    a.logits = p.logits;
+    a.stride = p.logits_stride_row;
+    a.mask_in = p.mask;
+    a.part = static_cast<Triple*>(ws);
+    a.B = p.B; a.S = p.S; a.V = p.V;
+    a.n_vsplit = pl.n_vsplit;
+    a.c = 1.44269504088896340736f;  // temperature 1
+    const dim3 grid(p.B * p.S, pl.n_vsplit);
+    if (p.dtype == TT_BF16) {
+        hipLaunchKernelGGL(vocab_reduce<true>, grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL(nll_finish<true>, dim3(1), dim3(256), 0, s, a, p.targets, p.nll, p.loss, p.count);
+    } else {
+        hipLaunchKernelGGL(vocab_reduce<false>, grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL(nll_finish<false>, dim3(1), dim3(256), 0, s, a, p.targets, p.nll, p.loss, p.count);
+    }
     return hipGetLastError() == hipSuccess ? TT_OK : TT_ERR_HIP;
 }
 

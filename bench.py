@@ -327,6 +327,55 @@ def run_append(args):
     return res
 
 
+NLL_METRIC = "masked positions scored per s (L_MD, Eq. 4); achieved HBM GB/s vs peak"
+
+
+def run_nll(args):
+    """L_MD (Eq. 4) over the denoise loop's logits: 32 x 16 positions, all masked, V = 131072, bf16.
+    Each call is timed between HIP events; the bytes are the logit rows read once."""
+    c = synth.unmask_case("loop")
+    targets = synth.spike_targets(c.B, c.S, c.V, seed=0, device="cuda").to(torch.int32)
+    x = synth.make_logits(c, seed=0, step=3, spike=1.5, targets=targets, device="cuda")
+    mask = torch.ones(c.B, c.S, dtype=torch.uint8, device="cuda")
+    nll = torch.empty(c.B, c.S, device="cuda")
+    loss = torch.zeros(1, device="cuda")
+    p = api.nll_params(x, targets, mask, nll=nll, loss=loss)
+    ws = torch.empty(max(16, api.lib().tt_masked_nll_workspace_bytes(p)), dtype=torch.uint8, device="cuda")
+    lib = api.lib()
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    for _ in range(args.warmup):
+        assert lib.tt_masked_nll(p, ws.data_ptr(), ws.numel(), sh) == 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        rc = lib.tt_masked_nll(p, ws.data_ptr(), ws.numel(), sh)
+        if rc:
+            raise RuntimeError(f"tt_masked_nll failed: {api.status_string(rc)}")
+    e1.record(stream)
+    torch.cuda.synchronize()
+    call_ms = e0.elapsed_time(e1) / args.steps
+    n = c.B * c.S
+    algo = n * c.V * 2 + n * (4 + 1 + 4)  # logit rows, targets, mask, nll
+    achieved = algo / (call_ms * 1e-3) / 1e9
+    res = {"metric": NLL_METRIC, "value": n / (call_ms * 1e-3), "unit": "positions/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": call_ms, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": f"masked NLL: B={c.B}, S={c.S}, V={c.V}, all masked", "global_batch": c.B,
+                      "seq_len": c.S, "parallelism": "none", "call_us": call_ms * 1e3, "loss": float(loss.item())},
+           "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": achieved / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes": algo}}
+    if not args.no_cpu:
+        import oracle
+        xs, ts, ms = x[:2].cpu(), targets[:2].cpu(), mask[:2].cpu()
+        t0 = time.perf_counter()
+        r = oracle.masked_nll(xs, ts, ms)
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": r["count"] / dt, "unit": "positions/s", "cores": 1, "kind": "oracle",
+                               "sample": f"2 of {c.B} sequences ({r['count']} positions)"}
+    return res
+
+
 def copy_calibration():
     """A plain device-to-device copy of COPY_BYTES, five times: the counter reference
     for FETCH_SIZE / WRITE_SIZE (each launch reads and writes COPY_BYTES)."""
@@ -343,7 +392,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="loop", choices=["loop", "single", "ragged", "long", "append"])
+    ap.add_argument("--workload", default="loop", choices=["loop", "single", "ragged", "long", "append", "nll"])
     ap.add_argument("--gamma", type=float, default=0.8)
     ap.add_argument("--temperature", type=float, default=0.1)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -364,6 +413,8 @@ def main():
         res = run_loop(args)
     elif args.workload == "append":
         res = run_append(args)
+    elif args.workload == "nll":
+        res = run_nll(args)
     else:
         res = run_single(args, args.workload)
     print(json.dumps(res))

@@ -17,6 +17,9 @@
  *   - tt_kv_append: section 2.1, Algorithm 1, the update of the AR context
  *     after a block is committed: the context cache of each attention layer
  *     grows by the committed block's keys and values.
+ *   - tt_masked_nll: section 2.2, Eq. (4), the masked-diffusion training loss
+ *     L_MD: the mean negative log-likelihood of the clean tokens over the
+ *     masked positions.
  *
  * Conventions shared by every call:
  *   - Pointers named as tensors are DEVICE pointers owned by the caller. The
@@ -272,6 +275,42 @@ typedef struct tt_kv_append_params {
 } tt_kv_append_params;
 
 tt_status tt_kv_append(const tt_kv_append_params* p, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * Masked negative log-likelihood L_MD (Eq. 4)
+ * ------------------------------------------------------------------------ *
+ * Section 2.2, Eq. (4): the denoiser is trained on the average negative
+ * log-likelihood of the clean token over the masked positions (the 1/t
+ * importance weight omitted). For each masked position (mask[b][l] != 0) with
+ * clean token y = targets[b][l] and logits x of row (b, l):
+ *   nll[b][l] = ln sum_v exp(x_v) - x_y            (softmax at temperature 1)
+ *   *loss     = sum of nll over masked positions / their number (0 if none)
+ *   *count    = the number of masked positions
+ * Rows of unmasked positions are not read and their nll is not written. A
+ * target outside [0, V) makes that row's nll (and the loss) NaN.
+ *
+ *   logits  [B][S][V] (dtype), row (b,l) at logits + (b*S + l)*logits_stride_row
+ *   targets [B][S] int32;  mask [B][S] uint8, 1 = masked
+ *   nll     [B][S] float32, optional;  loss: one device float32;  count: one
+ *           device int32, optional
+ * Requires B >= 0, S >= 1, V >= 1, logits_stride_row >= V, B*S below 2^31,
+ * logits aligned to its element size. Rows need at least one finite logit.
+ */
+typedef struct tt_masked_nll_params {
+    int32_t dtype; /* tt_dtype of logits */
+    int32_t B, S, V;
+    const void* logits;
+    int64_t logits_stride_row;
+    const int32_t* targets;
+    const uint8_t* mask;
+    float* nll;
+    float* loss;
+    int32_t* count;
+} tt_masked_nll_params;
+
+size_t tt_masked_nll_workspace_bytes(const tt_masked_nll_params* p);
+
+tt_status tt_masked_nll(const tt_masked_nll_params* p, void* workspace, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

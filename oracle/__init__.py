@@ -9,7 +9,8 @@ Each function follows the Nemotron-TwoTower paper (arXiv 2606.26493):
 Eq. (1)'s concatenated key set into disjoint parts, ``conf_unmask`` is the
 ConfidenceSample step of Algorithm 2 (section 2.2, "Sampling"),
 ``kv_append`` is the cache side of Algorithm 1's context update after a
-block is committed (section 2.1).
+block is committed (section 2.1), ``masked_nll`` is the loss L_MD of Eq. (4)
+(section 2.2).
 """
 from __future__ import annotations
 
@@ -53,6 +54,8 @@ def _bind(lib):
     lib.oracle_num_threads.restype = _I
     lib.oracle_kv_append.restype = _I
     lib.oracle_kv_append.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.oracle_masked_nll.restype = _I
+    lib.oracle_masked_nll.argtypes = [_I, _I, _I, _I, ctypes.c_longlong, _P, _P, _P, _P, _P, _P]
     return lib
 
 
@@ -214,6 +217,21 @@ def kv_append(Kc, Vc, page_table, ctx_len, Knew, Vnew, pool=None, pool_count=0):
                                  va.ctypes.data, pt.ctypes.data, cl.ctypes.data, kn.ctypes.data, vn.ctypes.data,
                                  pl.ctypes.data, pc.ctypes.data if pool is not None else None)
     return dict(Kc=Kt, Vc=Vt, page_table=pt, ctx_len=cl, pool_count=int(pc[0]), status=int(rc))
+
+
+def masked_nll(logits, targets, mask):
+    """L_MD of Eq. (4) in float64: returns dict(nll [B][S] (NaN where unmasked), loss, count)."""
+    B, S, V = logits.shape
+    la, lp, dt = _raw(logits)
+    tg = _i32(targets).reshape(B, S)
+    mk = np.ascontiguousarray(np.asarray(mask.cpu() if isinstance(mask, torch.Tensor) else mask, dtype=np.uint8))
+    nll = np.full((B, S), np.nan, np.float64)
+    loss = np.zeros(1, np.float64)
+    cnt = np.zeros(1, np.int32)
+    load().oracle_masked_nll(dt, B, S, V, V, lp, tg.ctypes.data, mk.ctypes.data, nll.ctypes.data, loss.ctypes.data,
+                             cnt.ctypes.data)
+    del la
+    return dict(nll=nll, loss=float(loss[0]), count=int(cnt[0]))
 
 
 def f32(x: float) -> float:

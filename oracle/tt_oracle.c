@@ -10,7 +10,8 @@
  * Source: "Nemotron-TwoTower: Diffusion Language Modeling with Pretrained
  * Autoregressive Context" (arXiv 2606.26493), section 2.1 "Bidirectional
  * attention", Eq. (1), and section 2.2 "Sampling", Algorithm 2; the
- * commit-time cache append follows Algorithm 1 of section 2.1.
+ * commit-time cache append follows Algorithm 1 of section 2.1, and the
+ * masked negative log-likelihood is Eq. (4) of section 2.2.
  *
  * Every function is the plain definition, written out in double precision
  * over the exactly decoded inputs (a bf16 value widened to double is exact).
@@ -301,5 +302,36 @@ int oracle_kv_append(int esz, int B, int S, int Hkv, int D, int page_size, int n
         ctx_len[b] = L + S;
     }
     if (needed > 0) *pool_count = count - needed;
+    return 0;
+}
+
+/* L_MD, Eq. (4) of section 2.2: for each masked position (mask != 0) with
+ * clean token y, -log p(y) = ln sum_v exp(x_v) - x_y (softmax at temperature
+ * 1, written with the row max m as m + ln sum_v exp(x_v - m)); loss is their
+ * mean over the masked positions, 0 when there are none. A target outside
+ * [0, V) gives NaN. nll_out is written for masked rows only. Returns 0. */
+int oracle_masked_nll(int dtype, int B, int S, int V, long long row_stride, const void* logits,
+                      const int* targets, const unsigned char* mask, double* nll_out, double* loss_out,
+                      int* count_out) {
+    double sum = 0.0;
+    int count = 0;
+    for (long long row = 0; row < (long long)B * S; ++row) {
+        if (!mask[row]) continue;
+        const size_t base = (size_t)row * (size_t)row_stride;
+        double m = -INFINITY;
+        for (int v = 0; v < V; ++v) {
+            const double x = ld(logits, base + v, dtype);
+            if (x > m) m = x;
+        }
+        double Z = 0.0;
+        for (int v = 0; v < V; ++v) Z += exp(ld(logits, base + v, dtype) - m);
+        const int y = targets[row];
+        const double nll = (y >= 0 && y < V) ? m + log(Z) - ld(logits, base + y, dtype) : NAN;
+        nll_out[row] = nll;
+        sum += nll;
+        ++count;
+    }
+    *loss_out = count > 0 ? sum / count : 0.0;
+    *count_out = count;
     return 0;
 }

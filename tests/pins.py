@@ -673,4 +673,82 @@ def pin_append_golden():
         assert torch.equal(r["Vc"], -r["Kc"]), c["name"]
 
 
+# ----------------------------------------------------------------------------
+# masked negative log-likelihood L_MD (Eq. 4)
+# ----------------------------------------------------------------------------
+
+def pin_nll_logsumexp():
+    """Per masked row, scipy's logsumexp minus the target logit; the loss is their mean over the
+    masked rows only; unmasked rows are left NaN."""
+    for dtype in (torch.float32, torch.bfloat16):
+        g = torch.Generator().manual_seed(21)
+        x = (torch.randn(3, 5, 777, generator=g) * 3).to(dtype)
+        t = torch.randint(0, 777, (3, 5), generator=g, dtype=torch.int32)
+        m = (torch.rand(3, 5, generator=g) < 0.6).to(torch.uint8)
+        m[0, 0] = 1
+        r = oracle.masked_nll(x, t, m)
+        xs = x.double().numpy()
+        want = []
+        for b in range(3):
+            for l in range(5):
+                if m[b, l]:
+                    v = scipy.special.logsumexp(xs[b, l]) - xs[b, l, int(t[b, l])]
+                    assert abs(r["nll"][b, l] - v) < 1e-9, (b, l)
+                    want.append(v)
+                else:
+                    assert math.isnan(r["nll"][b, l])
+        assert r["count"] == len(want)
+        assert abs(r["loss"] - math.fsum(want) / len(want)) < 1e-9
+
+
+def pin_nll_closed_forms():
+    """Uniform logits give ln V; a single finite logit at the target gives 0; a shift of every logit
+    changes nothing; two logits (a, b) with target a give ln(1 + e^(b-a))."""
+    V = 1000
+    x = torch.full((1, 2, V), 0.25)
+    r = oracle.masked_nll(x, torch.tensor([[3, 999]], dtype=torch.int32), torch.ones(1, 2, dtype=torch.uint8))
+    assert np.allclose(r["nll"], math.log(V), atol=1e-12, rtol=0)
+    x = torch.full((1, 1, 50), float("-inf"))
+    x[0, 0, 17] = 4.0
+    r = oracle.masked_nll(x, torch.tensor([[17]], dtype=torch.int32), torch.ones(1, 1, dtype=torch.uint8))
+    assert r["nll"][0, 0] == 0.0 and r["loss"] == 0.0
+    g = torch.Generator().manual_seed(22)
+    x = (torch.randn(2, 3, 64, generator=g, dtype=torch.float64) * 256).round().float() / 256  # k/256: +64 is exact
+    t = torch.randint(0, 64, (2, 3), generator=g, dtype=torch.int32)
+    mk = torch.ones(2, 3, dtype=torch.uint8)
+    a = oracle.masked_nll(x, t, mk)
+    b = oracle.masked_nll(x + 64.0, t, mk)  # exact in float32 at these magnitudes
+    assert np.allclose(a["nll"], b["nll"], atol=1e-9, rtol=0)
+    x = torch.tensor([[[1.5, -0.75]]])
+    r = oracle.masked_nll(x, torch.tensor([[0]], dtype=torch.int32), torch.ones(1, 1, dtype=torch.uint8))
+    assert abs(r["nll"][0, 0] - math.log1p(math.exp(-2.25))) < 1e-15
+
+
+def pin_nll_mask_and_targets():
+    """No masked position: count 0, loss 0. A target outside the vocabulary gives NaN."""
+    x = torch.randn(2, 4, 30)
+    t = torch.zeros(2, 4, dtype=torch.int32)
+    r = oracle.masked_nll(x, t, torch.zeros(2, 4, dtype=torch.uint8))
+    assert r["count"] == 0 and r["loss"] == 0.0 and np.isnan(r["nll"]).all()
+    t[1, 2] = 30
+    mk = torch.zeros(2, 4, dtype=torch.uint8)
+    mk[1, 2] = 1
+    r = oracle.masked_nll(x, t, mk)
+    assert r["count"] == 1 and math.isnan(r["nll"][1, 2]) and math.isnan(r["loss"])
+
+
+def pin_nll_golden():
+    """Hand-worked L_MD values (tests/golden/hand_cases.json, nll)."""
+    for c in json.load(open(GOLDEN))["nll"]:
+        r = oracle.masked_nll(torch.tensor(c["logits"], dtype=torch.float64).float(),
+                              torch.tensor(c["targets"], dtype=torch.int32), torch.tensor(c["mask"], dtype=torch.uint8))
+        for b, row in enumerate(c["expect_nll"]):
+            for l, v in enumerate(row):
+                if v is None:
+                    assert math.isnan(r["nll"][b, l])
+                else:
+                    assert abs(r["nll"][b, l] - v) < 1e-6, (c["name"], l)
+        assert abs(r["loss"] - c["expect_loss"]) < 1e-6 and r["count"] == c["expect_count"], c["name"]
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -11,7 +11,8 @@ import subprocess
 import pytest
 
 from attention_eq_block_amd import _lib
-from attention_eq_block_amd._lib import TT_BF16, TT_F32, BlockAttnParams, ConfUnmaskParams, KvAppendParams
+from attention_eq_block_amd._lib import (TT_BF16, TT_F32, BlockAttnParams, ConfUnmaskParams, KvAppendParams,
+                                         MaskedNllParams)
 
 FAKE = 0x1000  # never dereferenced: every call below must fail validation first
 
@@ -24,7 +25,8 @@ def test_library_loads_and_reports_version():
 def test_exports_every_header_function():
     names = _lib.header_functions()
     assert set(names) == {"tt_abi_version", "tt_status_string", "tt_block_attn", "tt_block_attn_workspace_bytes",
-                          "tt_lse_merge", "tt_conf_unmask", "tt_conf_unmask_workspace_bytes", "tt_kv_append"}
+                          "tt_lse_merge", "tt_conf_unmask", "tt_conf_unmask_workspace_bytes", "tt_kv_append",
+                          "tt_masked_nll", "tt_masked_nll_workspace_bytes"}
     L = _lib.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -190,3 +192,32 @@ def test_append_zero_batch_is_a_noop():
     L = _lib.lib()
     assert L.tt_kv_append(ctypes.byref(append_ok(B=0, Kctx=None, Knew=None, status=None)), None) == 0
     assert L.tt_kv_append(None, None) == 1
+
+
+def nll_ok(**kw):
+    p = MaskedNllParams()
+    p.dtype, p.B, p.S, p.V = TT_BF16, 4, 16, 131072
+    p.logits = p.targets = p.mask = p.loss = FAKE
+    p.logits_stride_row = 131072
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), 3), (dict(B=-1), 2), (dict(S=0), 2), (dict(V=0), 2), (dict(logits_stride_row=100), 2),
+    (dict(B=1 << 16, S=1 << 15), 2), (dict(logits=None), 1), (dict(targets=None), 1), (dict(mask=None), 1),
+    (dict(loss=None), 1), (dict(logits=FAKE + 1), 4), (dict(dtype=TT_F32, logits=FAKE + 2), 4),
+])
+def test_nll_validation(kw, code):
+    rc = _lib.lib().tt_masked_nll(ctypes.byref(nll_ok(**kw)), None, 0, None)
+    assert rc == code, (kw, _lib.STATUS.get(rc))
+
+
+def test_nll_needs_workspace_and_zero_batch_noop():
+    L = _lib.lib()
+    nb = L.tt_masked_nll_workspace_bytes(ctypes.byref(nll_ok()))
+    assert nb > 0
+    assert L.tt_masked_nll(ctypes.byref(nll_ok()), None, nb, None) == 5
+    assert L.tt_masked_nll(ctypes.byref(nll_ok(B=0, logits=None)), None, 0, None) == 0
+    assert L.tt_masked_nll(None, None, 0, None) == 1

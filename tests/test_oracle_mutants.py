@@ -55,6 +55,12 @@ MUTANTS = [
     ("append pool count kept", "if (needed > 0) *pool_count = count - needed;", ""),
     ("append new-row index transposed", "const size_t src = (((size_t)b * S + s) * Hkv + g) * row;",
      "const size_t src = (((size_t)s * B + b) * Hkv + g) * row;"),
+    ("nll without the max", "? m + log(Z) - ld(logits, base + y, dtype) : NAN;", "? log(Z) - ld(logits, base + y, dtype) : NAN;"),
+    ("nll target sign", "? m + log(Z) - ld(logits, base + y, dtype) : NAN;", "? m + log(Z) + ld(logits, base + y, dtype) : NAN;"),
+    ("nll mean over every row", "*loss_out = count > 0 ? sum / count : 0.0;",
+     "*loss_out = count > 0 ? sum / ((double)B * S) : 0.0;"),
+    ("nll at temperature 2", "Z += exp(ld(logits, base + v, dtype) - m);", "Z += exp((ld(logits, base + v, dtype) - m) / 2);"),
+    ("nll counts unmasked rows", "if (!mask[row]) continue;", "if (!mask[row] && row > 0) continue;"),
 ]
 
 
