@@ -81,6 +81,28 @@ def test_denoise_loop_teacher_forced(gamma):
     assert int(mask.sum()) == 0, "block must complete within T steps"
 
 
+@pytest.mark.parametrize("T", [16, 8, 4])
+def test_predict_and_noise_linear_schedule(T):
+    """The predict-and-noise sampler with low-confidence remasking (section 2.2; the schedule
+    alpha_t = 1 - t of Eq. (3)): every masked position is predicted and all but the ceil(M/R) most
+    confident are masked again, which is the step with gamma = +inf. With S divisible by T the block
+    then holds exactly S*(T - r)/T masked positions after step r, as the linear schedule says."""
+    c = synth.unmask_case("loop")
+    targets = synth.spike_targets(c.B, c.S, c.V, seed=0)
+    tokens, mask = synth.make_mask_state(c.B, c.S)
+    for r in range(1, T + 1):
+        x = synth.make_logits(c, seed=1, step=r, spike=0.5 * r, targets=targets)
+        # temperature 1: confidences stay well below 1 (no float32 saturation); every step is a top-k
+        # choice, so near-ties within 1e-6 are more frequent than at gamma < 1 and up to 15% of the
+        # sequences may be excluded from the exact comparison (the count check below covers all)
+        got, ref, skip = check_unmask(x, mask, tokens, gamma=float("inf"), temperature=1.0, steps_left=T - r + 1,
+                                      what=f"T={T} step {r}", max_fragile_frac=0.15)
+        assert np.all(got["num_masked"] == c.S * (T - r) // T), (r, got["num_masked"][:4])
+        tokens = torch.from_numpy(got["tokens"])
+        mask = torch.from_numpy(got["mask"])
+    assert int(mask.sum()) == 0
+
+
 @pytest.mark.parametrize("V", [1, 5, 8, 1000, 4099])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_vocab_sizes(V, dtype):
