@@ -216,6 +216,14 @@ def random_mask_state(B: int, S: int, p_masked: float, seed: int = 0, device="cp
     return tokens.to(device), mask.to(device)
 
 
+SUB_UNIFORM = 13
+
+
+def make_uniforms(B: int, S: int, seed: int = 0, step: int = 0, device="cpu") -> torch.Tensor:
+    """One float32 uniform in [0, 1) per block position, for the stochastic draw."""
+    return torch.rand((B, S), generator=_gen(seed, SUB_UNIFORM, 0, step)).to(device)
+
+
 # ----------------------------------------------------------------------------
 # commit-time cache append
 # ----------------------------------------------------------------------------

@@ -50,7 +50,7 @@ def _bind(lib):
     lib.oracle_lse_merge.argtypes = [_I, _I, _I, _P, _P, _P, _P]
     lib.oracle_conf_unmask.restype = _I
     lib.oracle_conf_unmask.argtypes = [_I, _I, _I, _I, ctypes.c_longlong, _P, _P, _P, ctypes.c_double,
-                                       ctypes.c_double, _I, _P, _P, _P, _P, _P]
+                                       ctypes.c_double, _I, _P, _P, _P, _P, _P, _P, _P]
     lib.oracle_num_threads.restype = _I
     lib.oracle_kv_append.restype = _I
     lib.oracle_kv_append.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P]
@@ -161,11 +161,15 @@ def lse_merge(O_parts, lse_parts):
     return O, L
 
 
-def conf_unmask(logits, mask, tokens, *, gamma: float, temperature: float, steps_left: int):
+def conf_unmask(logits, mask, tokens, *, gamma: float, temperature: float, steps_left: int, uniforms=None):
     """One ConfidenceSample step. ``gamma`` and ``temperature`` are used as given
-    (pass float32-rounded values to mirror a float32 caller).
+    (pass float32-rounded values to mirror a float32 caller). With ``uniforms``
+    ([B][S] float32 in [0, 1)) each masked row's token is drawn from
+    softmax(x / temperature) by inverse transform sampling instead of taken greedily.
 
-    Returns dict(tokens, mask, conf, argmax, num_masked) as numpy arrays.
+    Returns dict(tokens, mask, conf, argmax, margin, num_masked) as numpy arrays; ``argmax``
+    is the predicted token (greedy or drawn) and ``margin`` (sampling only, else None) the
+    distance of u from the cumulative values bracketing the drawn token.
     """
     B, S, V = logits.shape
     la, lp, dt = _raw(logits)
@@ -177,13 +181,19 @@ def conf_unmask(logits, mask, tokens, *, gamma: float, temperature: float, steps
     conf = np.zeros((B, S), np.float64)
     am = np.zeros((B, S), np.int32)
     nm = np.zeros((B,), np.int32)
+    un = margin = None
+    if uniforms is not None:
+        un = np.ascontiguousarray(np.asarray(uniforms.cpu() if isinstance(uniforms, torch.Tensor) else uniforms,
+                                             dtype=np.float32).reshape(B, S))
+        margin = np.full((B, S), np.nan, np.float64)
     rc = load().oracle_conf_unmask(dt, B, S, V, V, lp, mk.ctypes.data, tk.ctypes.data, float(gamma),
-                                   float(temperature), int(steps_left), tok_out.ctypes.data,
-                                   mask_out.ctypes.data, conf.ctypes.data, am.ctypes.data, nm.ctypes.data)
+                                   float(temperature), int(steps_left), None if un is None else un.ctypes.data,
+                                   tok_out.ctypes.data, mask_out.ctypes.data, conf.ctypes.data, am.ctypes.data,
+                                   None if margin is None else margin.ctypes.data, nm.ctypes.data)
     if rc != 0:
         raise ValueError("oracle_conf_unmask rejected its arguments")
     del la
-    return dict(tokens=tok_out, mask=mask_out, conf=conf, argmax=am, num_masked=nm)
+    return dict(tokens=tok_out, mask=mask_out, conf=conf, argmax=am, margin=margin, num_masked=nm)
 
 
 def kv_append(Kc, Vc, page_table, ctx_len, Knew, Vnew, pool=None, pool_count=0):

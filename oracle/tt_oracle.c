@@ -154,6 +154,43 @@ int oracle_lse_merge(int P, int n, int D, const double* O_parts, const double* l
     return 0;
 }
 
+/* Categorical draw from softmax(x / temperature) over one row of V logits
+ * starting at element base, by inverse transform sampling with uniform u:
+ * the cumulative sum C_v = e_0 + ... + e_v of e_v = exp((x_v - max x)/temperature)
+ * is compared with u * C_{V-1}. */
+static void draw_token(int dtype, const void* logits, size_t base, int V, double temperature, float uf,
+                       int32_t* tok, double* conf, double* margin) {
+    double u = (double)uf;
+    if (!(u > 0.0)) u = 0.0;
+    if (u > 1.0) u = 1.0;
+    double m = -INFINITY;
+    for (int v = 0; v < V; ++v) {
+        const double x = ld(logits, base + v, dtype);
+        if (x > m) m = x;
+    }
+    if (m == -INFINITY) { *tok = 0; *conf = NAN; if (margin) *margin = 0.0; return; }
+    double* e = (double*)malloc(sizeof(double) * (size_t)V);
+    double Z = 0.0;
+    for (int v = 0; v < V; ++v) {
+        e[v] = exp((ld(logits, base + v, dtype) - m) / temperature);
+        Z += e[v];
+    }
+    const double t = u * Z;
+    double C = 0.0, lo = 0.0, hi = 0.0, e_a = 0.0, C_last = 0.0;
+    int a = -1, last = -1;
+    for (int v = 0; v < V; ++v) {
+        const double Cn = C + e[v];
+        if (e[v] > 0.0) { last = v; C_last = C; }
+        if (a < 0 && Cn > t) { a = v; lo = C; hi = Cn; e_a = e[v]; }
+        C = Cn;
+    }
+    if (a < 0) { a = last; lo = C_last; e_a = e[last]; hi = C_last + e_a; }
+    free(e);
+    *tok = a;
+    *conf = e_a / Z;
+    if (margin) *margin = fmin(t - lo, hi - t) / Z;
+}
+
 /*
  * One ConfidenceSample step of Algorithm 2 (single-block confidence
  * unmasking), for B independent blocks of S positions.
@@ -169,20 +206,37 @@ int oracle_lse_merge(int P, int n, int D, const double* O_parts, const double* l
  * Committed positions take token a and leave the mask; all other positions,
  * and every already-unmasked position, are left untouched.
  *
+ * Stochastic variant (the sampler's temperature argument, section 2.2
+ * "Sampling"): when uniforms is not NULL, each masked row draws its token
+ * from p = softmax(x / temperature) by inverting the cumulative distribution
+ * in vocabulary order with the row's uniform u (clamped to [0, 1], NaN as 0):
+ * a = the smallest v with p_0 + ... + p_v > u, or, when no v qualifies
+ * (u = 1), the largest v with p_v > 0; its confidence is p_a. The commit rule
+ * is unchanged. margin_out (may be NULL) receives, per masked row, the
+ * distance of u from the nearer of the two cumulative values that bracket a,
+ * so that a caller can tell draws that rounding could move to a neighbour.
+ *
  * logits [B][S][V] (float32 or bf16, rows row_stride elements apart),
  * mask_in [B][S] (1 = masked), tokens_in [B][S] -> tokens_out, mask_out,
- * conf_out [B][S] (NaN where not masked), argmax_out [B][S] (-1 where not
- * masked), num_masked_out [B] (count after the step).
+ * conf_out [B][S] (NaN where not masked), argmax_out [B][S] (the predicted
+ * token: greedy or drawn; -1 where not masked), num_masked_out [B] (count
+ * after the step).
  */
 int oracle_conf_unmask(int dtype, int B, int S, int V, long long row_stride, const void* logits,
                        const uint8_t* mask_in, const int32_t* tokens_in, double gamma,
-                       double temperature, int steps_left, int32_t* tokens_out, uint8_t* mask_out,
-                       double* conf_out, int32_t* argmax_out, int32_t* num_masked_out) {
+                       double temperature, int steps_left, const float* uniforms, int32_t* tokens_out,
+                       uint8_t* mask_out, double* conf_out, int32_t* argmax_out, double* margin_out,
+                       int32_t* num_masked_out) {
     if (B < 0 || S < 1 || V < 1 || steps_left < 1 || !(temperature > 0.0) || gamma != gamma) return -1;
-    /* step 1: per masked row, greedy token and its confidence */
+    /* step 1: per masked row, the predicted token and its confidence */
 #pragma omp parallel for schedule(dynamic, 1)
     for (int row = 0; row < B * S; ++row) {
         if (!mask_in[row]) { conf_out[row] = NAN; argmax_out[row] = -1; continue; }
+        if (uniforms) {
+            draw_token(dtype, logits, (size_t)row * (size_t)row_stride, V, temperature, uniforms[row],
+                       &argmax_out[row], &conf_out[row], margin_out ? &margin_out[row] : NULL);
+            continue;
+        }
         const size_t base = (size_t)row * (size_t)row_stride;
         double m = -INFINITY;
         int a = 0;

@@ -751,4 +751,122 @@ def pin_nll_golden():
         assert abs(r["loss"] - c["expect_loss"]) < 1e-6 and r["count"] == c["expect_count"], c["name"]
 
 
+# ----------------------------------------------------------------------------
+# stochastic draw at temperature (section 2.2 "Sampling": the sampler's temperature argument)
+# ----------------------------------------------------------------------------
+
+def pin_sample_inverse_cdf_library():
+    """Drawn token = numpy.searchsorted(cumsum(scipy softmax(x/T)), u, 'right'), the first index whose
+    cumulative probability exceeds u; conf = that token's softmax probability. Rows whose u lies within
+    1e-12 of a bracketing cumulative value (where summation order could decide) are skipped."""
+    for temp in (1.0, 0.1, 0.37):
+        x = _tie_logits(4, 16, 997, seed=21)
+        tokens, mask = synth.make_mask_state(4, 16)
+        u = synth.make_uniforms(4, 16, seed=5)
+        r = oracle.conf_unmask(x, mask, tokens, gamma=0.5, temperature=temp, steps_left=4, uniforms=u)
+        p = scipy.special.softmax(x.double().numpy() / temp, axis=-1)
+        checked = 0
+        for b in range(4):
+            for l in range(16):
+                if r["margin"][b, l] < 1e-12:
+                    continue
+                want = int(np.searchsorted(np.cumsum(p[b, l]), float(u[b, l]), side="right"))
+                assert r["argmax"][b, l] == want, f"temperature {temp}: row ({b},{l}) drew {r['argmax'][b, l]}"
+                assert abs(r["conf"][b, l] - p[b, l, want]) < 1e-13, "conf must be the drawn token's probability"
+                checked += 1
+        assert checked >= 60
+
+
+def pin_sample_quadrature():
+    """On an evenly spaced grid of N uniforms the share of draws of each token is its softmax probability
+    to within 1/N, the drawn token never decreases as u grows, and -inf logits are never drawn."""
+    N = 4096
+    for temp, seed in ((1.0, 1), (0.25, 2), (3.0, 3)):
+        g = torch.Generator().manual_seed(seed)
+        row = torch.randn(23, generator=g) * 2
+        row[[4, 17]] = -math.inf
+        x = row.expand(1, N, 23).contiguous()
+        u = torch.tensor([[(i + 0.5) / N for i in range(N)]], dtype=torch.float32)
+        tokens, mask = synth.make_mask_state(1, N)
+        r = oracle.conf_unmask(x, mask, tokens, gamma=2.0, temperature=temp, steps_left=N, uniforms=u)
+        drawn = r["argmax"][0]
+        assert np.all(np.diff(drawn) >= 0), "the inverse transform must be monotone in u"
+        counts = np.bincount(drawn, minlength=23)
+        p = scipy.special.softmax(row.double().numpy() / temp)
+        assert counts[4] == 0 and counts[17] == 0, "a token of probability 0 was drawn"
+        assert np.all(np.abs(counts - N * p) <= 1.0 + 1e-9), f"temperature {temp}: {counts} vs {N * p}"
+
+
+def pin_sample_boundaries():
+    """Exact cases: two equal logits split [0, 1) at 1/2 with '>' (u = 1/2 draws the second token);
+    u = 0 draws the first token of nonzero probability and u = 1 the last one; NaN counts as 0."""
+    x = torch.tensor([[[0.0, 0.0], [0.0, 0.0], [0.0, 0.0]]])
+    tokens, mask = synth.make_mask_state(1, 3)
+    u = torch.tensor([[0.49999997, 0.5, 0.75]])
+    r = oracle.conf_unmask(x, mask, tokens, gamma=2.0, temperature=1.0, steps_left=8, uniforms=u)
+    assert r["argmax"][0].tolist() == [0, 1, 1], r["argmax"]
+    assert np.all(r["conf"][0] == 0.5)
+    x = torch.tensor([[[-math.inf, 0.0, 0.0, -math.inf]] * 4])
+    tokens, mask = synth.make_mask_state(1, 4)
+    u = torch.tensor([[0.0, 1.0, float("nan"), 0.5]])
+    r = oracle.conf_unmask(x, mask, tokens, gamma=2.0, temperature=1.0, steps_left=8, uniforms=u)
+    assert r["argmax"][0].tolist() == [1, 2, 1, 2], r["argmax"]
+
+
+def pin_sample_cold_limit():
+    """As the temperature goes to 0 the draw becomes the greedy argmax, whatever u is."""
+    g = torch.Generator().manual_seed(9)
+    x = torch.randn(2, 8, 300, generator=g)
+    top = x.argmax(-1, keepdim=True)
+    x.scatter_add_(2, top, torch.full((2, 8, 1), 0.5))     # a unique max, 0.5 clear of the rest
+    tokens, mask = synth.make_mask_state(2, 8)
+    u = synth.make_uniforms(2, 8, seed=3) * 0.999
+    r = oracle.conf_unmask(x, mask, tokens, gamma=0.5, temperature=1e-3, steps_left=8, uniforms=u)
+    assert np.array_equal(r["argmax"], top[..., 0].numpy())
+    assert np.all(np.abs(r["conf"] - 1.0) < 1e-12)
+
+
+def pin_sample_commit_rule():
+    """With drawn tokens the commit rule is the greedy one applied to the drawn tokens' probabilities:
+    the enumeration over subsets agrees, and committed positions take the drawn token."""
+    rng = np.random.default_rng(17)
+    for trial in range(40):
+        S = int(rng.integers(1, 8))
+        x = torch.tensor(rng.integers(-2, 3, size=(1, S, 4)).astype(np.float32))
+        mask = torch.tensor(rng.integers(0, 2, size=(1, S)).astype(np.uint8))
+        tokens = torch.tensor(rng.integers(100, 200, size=(1, S)).astype(np.int32))
+        u = torch.tensor(rng.random((1, S)).astype(np.float32))
+        gamma = float(rng.choice([-0.1, 0.3, 0.5, 1.0]))
+        R = int(rng.integers(1, 5))
+        r = oracle.conf_unmask(x, mask, tokens, gamma=gamma, temperature=1.0, steps_left=R, uniforms=u)
+        p = scipy.special.softmax(x[0].double().numpy(), axis=-1)
+        drawn = [int(np.searchsorted(np.cumsum(p[l]), float(u[0, l]), side="right")) for l in range(S)]
+        conf = [p[l, drawn[l]] for l in range(S)]
+        if any(r["margin"][0, l] < 1e-12 for l in range(S) if mask[0, l]):
+            continue
+        confs = sorted(conf[l] for l in range(S) if mask[0, l])
+        if any(b - a < 1e-12 and b != a for a, b in zip(confs, confs[1:])):
+            continue
+        want = _brute_commit(conf, mask[0].numpy(), gamma, R)
+        got = {l for l in range(S) if mask[0, l] and not r["mask"][0, l]}
+        assert got == want, f"trial {trial}: committed {sorted(got)}, enumeration says {sorted(want)}"
+        for l in want:
+            assert r["tokens"][0, l] == drawn[l], f"trial {trial}: token at {l}"
+
+
+def pin_sample_golden():
+    """Hand-worked stochastic steps (tests/golden/hand_cases.json, sample)."""
+    for c in json.load(open(GOLDEN))["sample"]:
+        x = torch.tensor(c["logits"], dtype=torch.float32)
+        r = oracle.conf_unmask(x, torch.tensor(c["mask"], dtype=torch.uint8),
+                               torch.tensor(c["tokens"], dtype=torch.int32), gamma=c["gamma"],
+                               temperature=c["temperature"], steps_left=c["steps_left"],
+                               uniforms=torch.tensor(c["uniforms"], dtype=torch.float32))
+        assert r["argmax"].tolist() == c["expect_drawn"], c["name"]
+        assert r["tokens"].tolist() == c["expect_tokens"], c["name"]
+        assert r["mask"].tolist() == c["expect_mask"], c["name"]
+        assert r["num_masked"].tolist() == c["expect_num_masked"], c["name"]
+        close(r["conf"], np.array(c["expect_conf"]), 1e-6, c["name"])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -59,6 +59,13 @@ MUTANTS = [
     ("nll target sign", "? m + log(Z) - ld(logits, base + y, dtype) : NAN;", "? m + log(Z) + ld(logits, base + y, dtype) : NAN;"),
     ("nll mean over every row", "*loss_out = count > 0 ? sum / count : 0.0;",
      "*loss_out = count > 0 ? sum / ((double)B * S) : 0.0;"),
+    ("sample cumulative not strict", "if (a < 0 && Cn > t) {", "if (a < 0 && Cn >= t) {"),
+    ("sample without temperature", "e[v] = exp((ld(logits, base + v, dtype) - m) / temperature);",
+     "e[v] = exp(ld(logits, base + v, dtype) - m);"),
+    ("sample conf of the max", "*conf = e_a / Z;", "*conf = 1.0 / Z;"),
+    ("sample fallback to the last index", "if (a < 0) { a = last;", "if (a < 0) { a = V - 1;"),
+    ("sample u not scaled by Z", "const double t = u * Z;", "const double t = u;"),
+    ("sample reversed order", "const double Cn = C + e[v];", "const double Cn = C + e[V - 1 - v];"),
     ("nll at temperature 2", "Z += exp(ld(logits, base + v, dtype) - m);", "Z += exp((ld(logits, base + v, dtype) - m) / 2);"),
     ("nll counts unmasked rows", "if (!mask[row]) continue;", "if (!mask[row] && row > 0) continue;"),
 ]
