@@ -43,7 +43,7 @@ class ConfUnmaskParams(ctypes.Structure):
         ("logits", c_ptr), ("logits_stride_row", c_i64),
         ("mask_in", c_ptr), ("mask_out", c_ptr), ("tokens", c_ptr),
         ("gamma", c_f32), ("temperature", c_f32), ("steps_left", c_i32),
-        ("conf", c_ptr), ("num_masked", c_ptr),
+        ("conf", c_ptr), ("num_masked", c_ptr), ("uniforms", c_ptr),
     ]
 
 

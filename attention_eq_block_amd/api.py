@@ -161,13 +161,16 @@ def lse_merge(O_parts: torch.Tensor, lse_parts: torch.Tensor, *, out: Optional[t
 
 
 def unmask_params(logits, mask_in, tokens, *, gamma: float, temperature: float, steps_left: int,
-                  mask_out=None, conf=None, num_masked=None) -> ConfUnmaskParams:
+                  mask_out=None, conf=None, num_masked=None, uniforms=None) -> ConfUnmaskParams:
     B, S, V = logits.shape
     if logits.stride(2) != 1 or logits.stride(0) != S * logits.stride(1):
         raise ValueError("logits rows must be evenly strided with the vocabulary contiguous")
     for t, name, dt in ((mask_in, "mask_in", torch.uint8), (tokens, "tokens", torch.int32)):
         if t.dtype != dt or not t.is_contiguous() or tuple(t.shape) != (B, S):
             raise ValueError(f"{name} must be dense {dt} [B][S]")
+    if uniforms is not None and (uniforms.dtype != torch.float32 or not uniforms.is_contiguous()
+                                 or tuple(uniforms.shape) != (B, S)):
+        raise ValueError("uniforms must be dense float32 [B][S]")
     p = ConfUnmaskParams()
     p.dtype = _code(logits)
     p.B, p.S, p.V = B, S, V
@@ -181,20 +184,23 @@ def unmask_params(logits, mask_in, tokens, *, gamma: float, temperature: float, 
     p.steps_left = int(steps_left)
     p.conf = _ptr(conf)
     p.num_masked = _ptr(num_masked)
+    p.uniforms = _ptr(uniforms)
     return p
 
 
 def conf_unmask(logits, mask_in, tokens, *, gamma: float, temperature: float = 1.0, steps_left: int = 1,
-                mask_out=None, conf=None, num_masked=None, workspace=None):
+                mask_out=None, conf=None, num_masked=None, uniforms=None, workspace=None):
     """One ConfidenceSample step, in place on ``tokens`` and ``mask_out`` (default: ``mask_in``).
 
     logits [B][S][V] bf16/f32; mask_in [B][S] uint8 (1 = masked); tokens [B][S] int32.
     Optional outputs: conf [B][S] float32 (masked rows), num_masked [B] int32.
+    uniforms [B][S] float32 in [0, 1): draw each token from softmax(x / temperature)
+    instead of taking the argmax (confidence = the drawn token's probability).
     Returns (tokens, mask_out).
     """
-    _need_cuda(logits, mask_in, tokens, mask_out, conf, num_masked, workspace)
+    _need_cuda(logits, mask_in, tokens, mask_out, conf, num_masked, uniforms, workspace)
     p = unmask_params(logits, mask_in, tokens, gamma=gamma, temperature=temperature, steps_left=steps_left,
-                      mask_out=mask_out, conf=conf, num_masked=num_masked)
+                      mask_out=mask_out, conf=conf, num_masked=num_masked, uniforms=uniforms)
     ws = _ws(int(lib().tt_conf_unmask_workspace_bytes(p)), logits.device, workspace)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     check(lib().tt_conf_unmask(p, _ptr(ws), nbytes, _stream(logits)), "tt_conf_unmask")

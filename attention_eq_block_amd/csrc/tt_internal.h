@@ -49,6 +49,7 @@ tt_status launch_lse_merge(int P, const float* O_parts, const float* lse_parts, 
 
 struct UnmaskPlan {
     int n_vsplit;
+    size_t ws_part;  // split triples; the drawn tokens follow when sampling
     size_t ws_total;
 };
 UnmaskPlan plan_unmask(const tt_conf_unmask_params& p, int n_cu);

@@ -10,6 +10,14 @@
 // position: confidence = 1/sum, then the commit rule -- every position above
 // gamma if there are at least ceil(M/steps_left) of them, else the
 // ceil(M/steps_left) most confident (ties to the lower position).
+// Stochastic variant (the sampler's temperature argument, section 2.2
+// "Sampling"), kernel 1b (sample_locate): a row with uniform u draws from
+// softmax(x / temperature) by inverse transform sampling. The split masses of
+// kernel 1 locate the split in which the cumulative sum passes u * Z; one
+// workgroup re-reads only that split, each thread a contiguous run of it, and a
+// workgroup scan of the run sums names the thread that walks its run again to
+// the first element whose cumulative sum passes. The drawn token's probability
+// replaces the greedy confidence in kernel 2.
 // The masked-diffusion loss L_MD (Eq. (4)) runs vocab_reduce at temperature 1
 // and a one-workgroup finish (nll_finish): lse - x[target] per masked row and
 // their mean.
@@ -29,6 +37,11 @@ struct Triple {
     float pad;
 };
 
+struct Drawn {
+    int a;
+    float conf;
+};
+
 struct UArgs {
     const void* logits;
     long long stride;
@@ -38,6 +51,8 @@ struct UArgs {
     float* conf;
     int* num_masked;
     Triple* part;  // [n_vsplit][B*S]
+    const float* uniforms;  // [B*S] or null (greedy)
+    Drawn* drawn;           // [B*S] when sampling
     int B, S, V, n_vsplit, steps_left;
     float gamma, c;  // c = log2(e) / temperature
 };
@@ -182,6 +197,173 @@ __global__ __launch_bounds__(256) void vocab_reduce(UArgs a) {
     }
 }
 
+// The 8 logits of 16-byte-aligned chunk ch of a row body, widened to float.
+template <bool BF16>
+__device__ __forceinline__ void load_chunk(const char* body, int ch, float (&f)[8]) {
+    if (BF16) {
+        unpack(*reinterpret_cast<const u32x4*>(body + (long long)ch * 16), f);
+    } else {
+        const u32x4 r0 = *reinterpret_cast<const u32x4*>(body + (long long)ch * 32);
+        const u32x4 r1 = *reinterpret_cast<const u32x4*>(body + (long long)ch * 32 + 16);
+        for (int e = 0; e < 4; ++e) { f[e] = __uint_as_float(r0[e]); f[4 + e] = __uint_as_float(r1[e]); }
+    }
+}
+
+// One thread's run of a split, in increasing index order: elements [0, head)
+// of the row, chunks [q0, q1) of the body (element a0 + 8 * chunk onwards),
+// then elements [tail0, tail1). Adds e_v = 2^(x_v c - m c) to s one element at a
+// time. With FIND it stops at the first element where base + s > r and returns
+// its index (e_hit = its e_v); it returns -1 otherwise. lastpos is the last
+// index seen with e_v > 0. Both instantiations perform the same additions in
+// the same order, so a run that passes r in the scan also passes it here.
+template <bool BF16, bool FIND>
+__device__ __forceinline__ int walk_run(const char* rp, const char* body, int a0, int head, int q0, int q1,
+                                        int tail0, int tail1, float c, float mc, float base, float r, float& s,
+                                        int& lastpos, float& e_hit) {
+    for (int v = 0; v < head; ++v) {
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(elem<BF16>(rp, v), c, -mc));
+        s += e;
+        if (e > 0.f) lastpos = v;
+        if (FIND && base + s > r) { e_hit = e; return v; }
+    }
+    // chunks in batches of 8 loads in flight; the additions stay in index order in both modes
+    int ch = q0;
+    for (; ch + 7 < q1; ch += 8) {
+        float f[8][8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) load_chunk<BF16>(body, ch + k, f[k]);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(f[k][j], c, -mc));
+                s += e;
+                if (e > 0.f) lastpos = a0 + (ch + k) * 8 + j;
+                if (FIND && base + s > r) { e_hit = e; return a0 + (ch + k) * 8 + j; }
+            }
+    }
+    for (; ch < q1; ++ch) {
+        float f[8];
+        load_chunk<BF16>(body, ch, f);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(f[j], c, -mc));
+            s += e;
+            if (e > 0.f) lastpos = a0 + ch * 8 + j;
+            if (FIND && base + s > r) { e_hit = e; return a0 + ch * 8 + j; }
+        }
+    }
+    for (int v = tail0; v < tail1; ++v) {
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(elem<BF16>(rp, v), c, -mc));
+        s += e;
+        if (e > 0.f) lastpos = v;
+        if (FIND && base + s > r) { e_hit = e; return v; }
+    }
+    return -1;
+}
+
+// Inverse transform draw for every masked row (one workgroup of 256 threads
+// per row), after vocab_reduce has written the split triples.
+template <bool BF16>
+__global__ __launch_bounds__(256) void sample_locate(UArgs a) {
+    const int row = blockIdx.x;
+    if (!a.mask_in[row]) return;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const long long rows = (long long)a.B * a.S;
+    const float c = a.c;
+    __shared__ float sh_m, sh_z, sh_r;
+    __shared__ int sh_k, sh_am;
+    __shared__ float wsum[4];
+    __shared__ int wfirst[4], wlast[4];
+    if (tid == 0) {
+        float m = -INFINITY, z = 0.f;
+        int am = INT_MAX;
+        for (int k = 0; k < a.n_vsplit; ++k) {
+            const Triple t = a.part[(long long)k * rows + row];
+            combine(m, am, z, t.m, t.a, t.z, c);
+        }
+        float u = a.uniforms[row];
+        u = u > 0.f ? fminf(u, 1.f) : 0.f;  // NaN and negatives count as 0
+        const float t = u * z;
+        int kk = -1, klast = -1;
+        float W = 0.f, r = INFINITY;
+        if (m != -INFINITY) {
+            for (int k = 0; k < a.n_vsplit; ++k) {
+                const Triple tr = a.part[(long long)k * rows + row];
+                const float wk = tr.m == -INFINITY ? 0.f : tr.z * __builtin_amdgcn_exp2f((tr.m - m) * c);
+                if (wk > 0.f) klast = k;
+                if (kk < 0 && W + wk > t) { kk = k; r = t - W; }
+                W += wk;
+            }
+            if (kk < 0) kk = klast;
+        }
+        sh_m = m; sh_z = z; sh_r = r; sh_k = kk; sh_am = am;
+    }
+    __syncthreads();
+    const int k = sh_k;
+    if (k < 0) {  // no logit of nonzero weight: the greedy result stands
+        if (tid == 0) a.drawn[row] = Drawn{sh_am, 1.f / sh_z};
+        return;
+    }
+    const float m = sh_m, z = sh_z, r = sh_r, mc = m * c;
+    // the split's extent, cut exactly as in vocab_reduce
+    constexpr int ES = BF16 ? 2 : 4;
+    const char* rp = static_cast<const char*>(a.logits) + (long long)row * a.stride * ES;
+    int a0 = (int)(((16u - (unsigned)(reinterpret_cast<uintptr_t>(rp) & 15u)) & 15u) / ES);
+    if (a0 > a.V) a0 = a.V;
+    const int nfull = (a.V - a0) / 8;
+    const int per = (nfull + a.n_vsplit - 1) / a.n_vsplit;
+    const int c0 = min(nfull, k * per), c1 = min(nfull, c0 + per);
+    const int q = (c1 - c0 + 255) / 256;
+    const int q0 = min(c1, c0 + tid * q), q1 = min(c1, q0 + q);
+    const int head = (k == 0 && tid == 0) ? a0 : 0;
+    const int tail0 = a0 + nfull * 8;
+    const int tail1 = (k == a.n_vsplit - 1 && tid == 255) ? a.V : tail0;
+    const char* body = rp + a0 * ES;
+    float s = 0.f, e_hit = 0.f;
+    int lastpos = -1;
+    walk_run<BF16, false>(rp, body, a0, head, q0, q1, tail0, tail1, c, mc, 0.f, 0.f, s, lastpos, e_hit);
+    // workgroup exclusive scan of the run sums, in thread order
+    float incl = s;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+    }
+    float excl = __shfl_up(incl, 1);
+    if (lane == 0) excl = 0.f;
+    int lp = lastpos;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) lp = max(lp, __shfl_xor(lp, off));
+    if (lane == 63) wsum[w] = incl;
+    if (lane == 0) wlast[w] = lp;
+    __syncthreads();
+    float wb = 0.f;
+    for (int j = 0; j < w; ++j) wb += wsum[j];
+    const float base = wb + excl;
+    const unsigned long long hit = __ballot(base + s > r);
+    if (lane == 0) wfirst[w] = hit ? w * 64 + __builtin_ctzll(hit) : INT_MAX;
+    __syncthreads();
+    const int first = min(min(wfirst[0], wfirst[1]), min(wfirst[2], wfirst[3]));
+    if (first == INT_MAX) {
+        // u * Z not passed inside the split (u = 1, or rounding): its last element of nonzero weight
+        if (tid == 0) {
+            const int last = max(max(wlast[0], wlast[1]), max(wlast[2], wlast[3]));
+            if (last < 0) {
+                a.drawn[row] = Drawn{sh_am, 1.f / z};
+            } else {
+                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(elem<BF16>(rp, last), c, -mc));
+                a.drawn[row] = Drawn{last, e / z};
+            }
+        }
+    } else if (tid == first) {
+        float s2 = 0.f;
+        int lp2 = -1;
+        const int v = walk_run<BF16, true>(rp, body, a0, head, q0, q1, tail0, tail1, c, mc, base, r, s2, lp2, e_hit);
+        a.drawn[row] = v >= 0 ? Drawn{v, e_hit / z} : Drawn{sh_am, 1.f / z};
+    }
+}
+
 __global__ __launch_bounds__(64) void unmask_select(UArgs a) {
     const int b = blockIdx.x;
     const int l = threadIdx.x;
@@ -196,7 +378,12 @@ __global__ __launch_bounds__(64) void unmask_select(UArgs a) {
             combine(m, am, z, t.m, t.a, t.z, a.c);
         }
     }
-    const float conf = masked ? 1.f / z : -INFINITY;
+    float conf = masked ? 1.f / z : -INFINITY;
+    if (masked && a.drawn) {
+        const Drawn d = a.drawn[row];
+        am = d.a;
+        conf = d.conf;
+    }
     const unsigned long long mmask = __ballot(masked);
     const int M = __popcll(mmask);
     const int kmin = (M + a.steps_left - 1) / a.steps_left;
@@ -282,7 +469,8 @@ UnmaskPlan plan_unmask(const tt_conf_unmask_params& p, int n_cu) {
     if (want < 1) want = 1;
     if (want > 64) want = 64;
     pl.n_vsplit = (int)want;
-    pl.ws_total = (size_t)pl.n_vsplit * (size_t)rows * sizeof(Triple);
+    pl.ws_part = (size_t)pl.n_vsplit * (size_t)rows * sizeof(Triple);
+    pl.ws_total = pl.ws_part + (p.uniforms ? (size_t)rows * sizeof(Drawn) : 0);
     return pl;
 }
 
@@ -301,11 +489,19 @@ tt_status launch_unmask(const tt_conf_unmask_params& p, const UnmaskPlan& pl, vo
     a.steps_left = p.steps_left;
     a.gamma = p.gamma;
     a.c = 1.44269504088896340736f / p.temperature;
+    a.uniforms = p.uniforms;
+    a.drawn = p.uniforms ? reinterpret_cast<Drawn*>(static_cast<char*>(ws) + pl.ws_part) : nullptr;
     const dim3 grid(p.B * p.S, pl.n_vsplit);
     if (p.dtype == TT_BF16)
         hipLaunchKernelGGL(vocab_reduce<true>, grid, dim3(256), 0, s, a);
     else
         hipLaunchKernelGGL(vocab_reduce<false>, grid, dim3(256), 0, s, a);
+    if (p.uniforms) {
+        if (p.dtype == TT_BF16)
+            hipLaunchKernelGGL(sample_locate<true>, dim3(p.B * p.S), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL(sample_locate<false>, dim3(p.B * p.S), dim3(256), 0, s, a);
+    }
     hipLaunchKernelGGL(unmask_select, dim3(p.B), dim3(64), 0, s, a);
     return hipGetLastError() == hipSuccess ? TT_OK : TT_ERR_HIP;
 }

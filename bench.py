@@ -328,6 +328,7 @@ def run_append(args):
 
 
 NLL_METRIC = "masked positions scored per s (L_MD, Eq. 4); achieved HBM GB/s vs peak"
+SAMPLE_METRIC = "masked rows per s of the stochastic unmask step (temperature draw); achieved HBM GB/s vs peak"
 
 
 def run_nll(args):
@@ -376,6 +377,64 @@ def run_nll(args):
     return res
 
 
+def run_sample(args):
+    """One ConfidenceSample step with the stochastic draw (caller uniforms) on the denoise loop's
+    first-step logits: 32 x 16 positions, all masked, V = 131072 bf16, gamma and temperature as
+    given, 16 steps left. Each call is timed between HIP events (mask_out is a separate buffer, so
+    every call sees the same all-masked state); the greedy step is timed the same way beside it.
+    The bytes are the masked logit rows read once, as for the greedy step."""
+    c = synth.unmask_case("loop")
+    targets = synth.spike_targets(c.B, c.S, c.V, seed=0, device="cuda")
+    x = synth.make_logits(c, seed=0, step=1, spike=0.5, targets=targets, device="cuda")
+    mask = torch.ones(c.B, c.S, dtype=torch.uint8, device="cuda")
+    mask_out = torch.empty_like(mask)
+    tokens = torch.full((c.B, c.S), synth.MASK_TOKEN_ID, dtype=torch.int32, device="cuda")
+    u = synth.make_uniforms(c.B, c.S, seed=0, step=1, device="cuda")
+    lib = api.lib()
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def timed(uniforms):
+        p = api.unmask_params(x, mask, tokens, gamma=args.gamma, temperature=args.temperature, steps_left=16,
+                              mask_out=mask_out, uniforms=uniforms)
+        ws = torch.empty(max(16, api.conf_unmask_workspace_bytes(p)), dtype=torch.uint8, device="cuda")
+        for _ in range(args.warmup):
+            assert lib.tt_conf_unmask(p, ws.data_ptr(), ws.numel(), sh) == 0
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            rc = lib.tt_conf_unmask(p, ws.data_ptr(), ws.numel(), sh)
+            if rc:
+                raise RuntimeError(f"tt_conf_unmask failed: {api.status_string(rc)}")
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    greedy_ms = timed(None)
+    call_ms = timed(u)
+    n = c.B * c.S
+    algo = n * c.V * 2 + n * (4 + 1 + 1 + 4 + 4)  # logit rows, uniform, mask in/out, token, conf
+    achieved = algo / (call_ms * 1e-3) / 1e9
+    res = {"metric": SAMPLE_METRIC, "value": n / (call_ms * 1e-3), "unit": "masked rows/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": call_ms, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": f"stochastic unmask step: B={c.B}, S={c.S}, V={c.V}, all masked, "
+                                  f"gamma {args.gamma}, temperature {args.temperature}",
+                      "global_batch": c.B, "seq_len": c.S, "parallelism": "none", "call_us": call_ms * 1e3,
+                      "greedy_call_us": greedy_ms * 1e3},
+           "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": achieved / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes": algo}}
+    if not args.no_cpu:
+        import oracle
+        xs, ms, ts, us = x[:2].cpu(), mask[:2].cpu(), tokens[:2].cpu(), u[:2].cpu()
+        t0 = time.perf_counter()
+        oracle.conf_unmask(xs, ms, ts, gamma=args.gamma, temperature=args.temperature, steps_left=16, uniforms=us)
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": 2 * c.S / dt, "unit": "masked rows/s", "cores": oracle.num_threads(),
+                               "kind": "oracle", "sample": f"2 of {c.B} sequences ({2 * c.S} masked rows)"}
+    return res
+
+
 def copy_calibration():
     """A plain device-to-device copy of COPY_BYTES, five times: the counter reference
     for FETCH_SIZE / WRITE_SIZE (each launch reads and writes COPY_BYTES)."""
@@ -392,7 +451,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="loop", choices=["loop", "single", "ragged", "long", "append", "nll"])
+    ap.add_argument("--workload", default="loop", choices=["loop", "single", "ragged", "long", "append", "nll", "sample"])
     ap.add_argument("--gamma", type=float, default=0.8)
     ap.add_argument("--temperature", type=float, default=0.1)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -413,6 +472,8 @@ def main():
         res = run_loop(args)
     elif args.workload == "append":
         res = run_append(args)
+    elif args.workload == "sample":
+        res = run_sample(args)
     elif args.workload == "nll":
         res = run_nll(args)
     else:

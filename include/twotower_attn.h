@@ -198,6 +198,18 @@ tt_status tt_lse_merge(int P, const float* O_parts, const float* lse_parts, int 
  * Requires 1 <= S <= 64, V >= 1, logits_stride_row >= V, gamma not NaN,
  * temperature finite and > 0, steps_left >= 1. Rows must hold at least one
  * finite logit; -inf logits have probability 0.
+ *
+ * Stochastic draw (the sampler's temperature argument, section 2.2
+ * "Sampling"): when uniforms is not NULL, a_l is drawn from
+ * p = softmax(x / temperature) instead of taken greedily, by inverse transform
+ * sampling with u = uniforms[b][l]: a_l is the smallest v whose cumulative
+ * probability p_0 + ... + p_v exceeds u (the largest v with p_v > 0 when none
+ * does), and conf_l = p_{a_l}. The commit rule is unchanged.
+ *   uniforms [B][S] float32 device array, optional; values outside [0, 1] are
+ *            clamped to it and NaN counts as 0. The caller owns the generator:
+ *            the library draws no random numbers. The cumulative sums are
+ *            float32, so a u within about 1e-5 of a cumulative value may select
+ *            the neighbouring token.
  */
 typedef struct tt_conf_unmask_params {
     int32_t dtype;  /* tt_dtype of logits */
@@ -212,6 +224,7 @@ typedef struct tt_conf_unmask_params {
     int32_t steps_left;
     float* conf;
     int32_t* num_masked;
+    const float* uniforms;
 } tt_conf_unmask_params;
 
 size_t tt_conf_unmask_workspace_bytes(const tt_conf_unmask_params* p);

@@ -103,7 +103,8 @@ def check_attn_rows(O_gpu, L_gpu, inp, rows, dtype, what=""):
 # confidence unmask
 # ---------------------------------------------------------------------------
 
-def gpu_unmask(logits, mask, tokens, *, gamma, temperature, steps_left, separate_out=False, want_conf=True):
+def gpu_unmask(logits, mask, tokens, *, gamma, temperature, steps_left, separate_out=False, want_conf=True,
+               uniforms=None):
     lg = logits.cuda()
     mk = mask.cuda().clone()
     tk = tokens.cuda().clone()
@@ -111,8 +112,9 @@ def gpu_unmask(logits, mask, tokens, *, gamma, temperature, steps_left, separate
     conf = torch.full((B, S), float("nan"), device="cuda") if want_conf else None
     nm = torch.full((B,), -7, dtype=torch.int32, device="cuda")
     mo = torch.full_like(mk, 77) if separate_out else None
+    un = None if uniforms is None else uniforms.cuda()
     api.conf_unmask(lg, mk, tk, gamma=gamma, temperature=temperature, steps_left=steps_left, mask_out=mo,
-                    conf=conf, num_masked=nm)
+                    conf=conf, num_masked=nm, uniforms=un)
     torch.cuda.synchronize()
     out_mask = mo if separate_out else mk
     return dict(tokens=tk.cpu().numpy(), mask=out_mask.cpu().numpy(), num_masked=nm.cpu().numpy(),
@@ -140,16 +142,68 @@ def fragile(ref_conf, mask, gamma, steps_left, eps=1e-6):
     return out
 
 
+# The kernel's cumulative probabilities are float32 sums of up to 131072 terms (runs of a few hundred
+# terms added in order, then a scan and the split masses): their error is of order 1e-6 of the total
+# and below 256 * 2^-24 = 1.5e-5 in the worst case. A drawn token is valid when it is the exact
+# inverse-transform draw for some uniform within DRAW_TOL of the given one. At temperature 1 over
+# 131072 tokens each probability is about 7.6e-6, so the float32 and float64 draws often differ by
+# a neighbour; that is the float32 rounding, not a different method.
+DRAW_TOL = 3e-5
+
+
+def settle_uniforms(logits, mask, uniforms, temperature, drawn):
+    """Check every GPU draw against the exact float64 cumulative distribution and return uniforms
+    that make the oracle draw the GPU's tokens: u itself where the GPU's token is the exact draw
+    for u with room to spare, else the middle of the GPU token's bracket (after checking that u is
+    within DRAW_TOL of that bracket). Also returns the number of moved uniforms and, per sequence,
+    whether no float32 uniform could reproduce a draw (then the sequence is excluded)."""
+    x = logits.float().numpy() if isinstance(logits, torch.Tensor) else np.asarray(logits, np.float32)
+    B, S = mask.shape
+    t = float(oracle.f32(temperature))
+    u = uniforms.cpu().numpy().astype(np.float32).copy()
+    moved, bad = 0, np.zeros(B, dtype=bool)
+    for b, l in zip(*np.nonzero(mask)):
+        z = x[b, l].astype(np.float64) / t
+        e = np.exp(z - z.max())
+        C = np.cumsum(e)
+        a = int(drawn[b, l])
+        assert 0 <= a < C.size and e[a] > 0, f"row ({b},{l}): drew token {a} of probability 0"
+        lo = C[a - 1] / C[-1] if a > 0 else 0.0
+        hi = C[a] / C[-1]
+        uu = float(u[b, l])
+        uu = 0.0 if not uu > 0 else min(uu, 1.0)
+        assert lo - DRAW_TOL <= uu <= hi + DRAW_TOL, \
+            f"row ({b},{l}): token {a} has bracket [{lo:.9f}, {hi:.9f}) but u = {uu:.9f}"
+        if lo + 1e-9 < uu < hi - 1e-9:
+            continue
+        mid = np.float32((lo + hi) / 2)
+        if lo + 1e-9 < float(mid) < hi - 1e-9:
+            u[b, l] = mid
+            moved += 1
+        else:
+            bad[b] = True
+    return torch.from_numpy(u), moved, bad
+
+
 def check_unmask(logits, mask, tokens, *, gamma, temperature, steps_left, separate_out=False, what="",
-                 max_fragile_frac=0.05):
+                 max_fragile_frac=0.05, uniforms=None):
     """Run both sides from the same state and compare to the bar; returns the GPU result."""
     g32 = oracle.f32(gamma)
     t32 = oracle.f32(temperature)
-    ref = oracle.conf_unmask(logits, mask, tokens, gamma=g32, temperature=t32, steps_left=steps_left)
-    got = gpu_unmask(logits, mask, tokens, gamma=gamma, temperature=temperature, steps_left=steps_left,
-                     separate_out=separate_out)
     mk = mask.cpu().numpy()
-    skip = fragile(ref["conf"], mk, g32, steps_left)
+    bad = np.zeros(mk.shape[0], dtype=bool)
+    u_ref = uniforms
+    if uniforms is not None:
+        # every draw, made visible by committing all positions (the draws do not depend on gamma)
+        every = gpu_unmask(logits, mask, tokens, gamma=-1.0, temperature=temperature, steps_left=1,
+                           want_conf=False, uniforms=uniforms)
+        u_ref, moved, bad = settle_uniforms(logits, mk, uniforms, temperature, every["tokens"])
+        print(f"{what}: {moved} of {int(mk.sum())} draws settled on a float32 neighbour within {DRAW_TOL}")
+    ref = oracle.conf_unmask(logits, mask, tokens, gamma=g32, temperature=t32, steps_left=steps_left,
+                             uniforms=u_ref)
+    got = gpu_unmask(logits, mask, tokens, gamma=gamma, temperature=temperature, steps_left=steps_left,
+                     separate_out=separate_out, uniforms=uniforms)
+    skip = fragile(ref["conf"], mk, g32, steps_left) | bad
     assert skip.mean() <= max_fragile_frac, f"{what}: {skip.sum()} of {len(skip)} sequences fragile"
     keep = ~skip
     assert np.array_equal(got["tokens"][keep], ref["tokens"][keep]), f"{what}: tokens differ"
@@ -157,9 +211,10 @@ def check_unmask(logits, mask, tokens, *, gamma, temperature, steps_left, separa
     assert np.array_equal(got["num_masked"][keep], ref["num_masked"][keep]), f"{what}: num_masked differ"
     m = mk.astype(bool)
     dc = np.abs(got["conf"][m] - ref["conf"][m])
-    assert np.all(dc <= 1e-6 + 1e-5 * ref["conf"][m]), f"{what}: conf max err {dc.max():.3e}"
+    assert np.all(dc <= 1e-6 + 1e-5 * ref["conf"][m]), f"{what}: conf max err {dc.max() if dc.size else 0:.3e}"
     # rows that were not masked: conf untouched (NaN sentinel), tokens untouched
-    assert np.all(np.isnan(got["conf"][~m])), f"{what}: conf written at unmasked rows"
+    um = ~mk.astype(bool)
+    assert np.all(np.isnan(got["conf"][um])), f"{what}: conf written at unmasked rows"
     tk = tokens.cpu().numpy()
-    assert np.array_equal(got["tokens"][~m], tk[~m]), f"{what}: unmasked tokens changed"
+    assert np.array_equal(got["tokens"][um], tk[um]), f"{what}: unmasked tokens changed"
     return got, ref, skip

@@ -1,0 +1,123 @@
+"""tt_conf_unmask with caller uniforms (the stochastic draw at temperature of Nemotron-TwoTower
+section 2.2 "Sampling", inside Algorithm 2's ConfidenceSample step) on the GPU against the
+float64 oracle. Every GPU draw must be the exact inverse-transform draw for a uniform within
+3e-5 of the given one (float32 cumulative sums); the oracle then runs with uniforms that draw the
+GPU's tokens, and tokens, masks and counts are compared bit for bit, excluding sequences with a
+decision within 1e-6 of gamma or of the fallback cut (parity.py)."""
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+from attention_eq_block_amd import synth
+
+from parity import check_unmask, gpu_unmask
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("temperature", [1.0, 0.1])
+def test_sample_tiny_fp32(temperature):
+    """Logits 16 x 1024 float32, N(0,1) + 4 at a seeded token, all masked, gamma 0.8."""
+    c = synth.unmask_case("tiny", temperature=temperature)
+    x = synth.make_logits(c, seed=0)
+    tokens, mask = synth.make_mask_state(c.B, c.S)
+    u = synth.make_uniforms(c.B, c.S, seed=0)
+    check_unmask(x, mask, tokens, gamma=0.8, temperature=temperature, steps_left=16, uniforms=u,
+                 what="tiny", max_fragile_frac=1.0)
+
+
+@pytest.mark.parametrize("temperature", [0.1, 1.0])
+def test_sample_ragged_full_size(temperature):
+    """64 x 16 x 131072 bf16 logits, N(0,1) + U(0,8) spike per row, all masked, gamma 0.8, R = 16."""
+    c = synth.unmask_case("ragged", temperature=temperature)
+    x = synth.make_logits(c, seed=0)
+    tokens, mask = synth.make_mask_state(c.B, c.S)
+    u = synth.make_uniforms(c.B, c.S, seed=1)
+    got, ref, skip = check_unmask(x, mask, tokens, gamma=0.8, temperature=temperature, steps_left=16,
+                                  uniforms=u, what=f"ragged T={temperature}")
+    drawn_not_greedy = int((ref["argmax"] != np.argmax(x.float().numpy(), axis=-1)).sum())
+    print(f"excluded {skip.sum()} of {len(skip)}; draws off the argmax {drawn_not_greedy}")
+    if temperature == 1.0:
+        assert drawn_not_greedy > 100, "at temperature 1 most draws leave the argmax"
+
+
+def test_sample_denoise_loop_teacher_forced():
+    """Algorithm 2 on the loop workload (32 x 16 x 131072, spike 0.5*t at step t, T = 16, gamma 0.8,
+    temperature 0.1) with fresh uniforms each step; each step is compared with the oracle run from
+    the GPU's own input state, and the block completes within T steps."""
+    c = synth.unmask_case("loop", gamma=0.8)
+    targets = synth.spike_targets(c.B, c.S, c.V, seed=0)
+    tokens, mask = synth.make_mask_state(c.B, c.S)
+    T = synth.LOOP_STEPS
+    for r in range(1, T + 1):
+        x = synth.make_logits(c, seed=0, step=r, spike=0.5 * r, targets=targets)
+        u = synth.make_uniforms(c.B, c.S, seed=0, step=r)
+        got, ref, skip = check_unmask(x, mask, tokens, gamma=0.8, temperature=0.1, steps_left=T - r + 1,
+                                      uniforms=u, what=f"loop step {r}")
+        tokens = torch.from_numpy(got["tokens"])
+        mask = torch.from_numpy(got["mask"])
+        if int(mask.sum()) == 0:
+            break
+    assert int(mask.sum()) == 0, "block must complete within T steps"
+
+
+@pytest.mark.parametrize("V", [1, 5, 8, 1000, 4099])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_sample_vocab_sizes(V, dtype):
+    """Vocabularies that are tiny, not a multiple of 8, or leave a ragged last chunk; random masks."""
+    g = torch.Generator().manual_seed(V)
+    x = (torch.randn(3, 9, V, generator=g) * 2).to(dtype)
+    tokens, mask = synth.random_mask_state(3, 9, 0.8, seed=V)
+    for R in (1, 3, 9):
+        u = synth.make_uniforms(3, 9, seed=V, step=R)
+        check_unmask(x, mask, tokens, gamma=0.3, temperature=0.7, steps_left=R, uniforms=u,
+                     what=f"V={V} R={R}", max_fragile_frac=0.34)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_sample_strided_rows_many_splits(dtype):
+    """Rows 100043 elements apart starting off a 16-byte boundary (a head before the first aligned
+    chunk, a ragged tail), V = 100000 over 10 rows, so the vocabulary is cut into many splits."""
+    base = torch.randn(2, 5, 100043, generator=torch.Generator().manual_seed(4)).to(dtype)
+    x = base[:, :, 3:100003]
+    tokens, mask = synth.make_mask_state(2, 5)
+    for temp, seed in ((1.0, 1), (0.2, 2), (5.0, 3)):
+        u = synth.make_uniforms(2, 5, seed=seed)
+        check_unmask(x, mask, tokens, gamma=0.5, temperature=temp, steps_left=5, uniforms=u,
+                     what=f"strided T={temp}", max_fragile_frac=0.5)
+
+
+def test_sample_exact_boundaries():
+    """Exact arithmetic on both sides: two equal logits split [0, 1) at 1/2 ('>' draws the second
+    token at u = 1/2); u = 0 draws the first token of nonzero probability, u = 1 the last, NaN
+    counts as 0, and -inf logits are never drawn."""
+    x = torch.tensor([[[-math.inf, 0.0, 0.0, -math.inf]] * 6])
+    tokens, mask = synth.make_mask_state(1, 6)
+    u = torch.tensor([[0.0, 1.0, float("nan"), 0.5, 0.49999997, -3.0]])
+    got = gpu_unmask(x, mask, tokens, gamma=2.0, temperature=1.0, steps_left=1, uniforms=u)
+    assert got["tokens"][0].tolist() == [1, 2, 1, 2, 1, 1], got["tokens"]
+    assert np.all(got["conf"][0] == 0.5)
+
+
+def test_sample_grid_frequencies():
+    """4096 positions share one row (V = 50, temperature 0.5) and take the uniforms (i + 1/2)/4096:
+    each token is drawn (4096 times its softmax probability) times, to within one draw plus the
+    draws whose uniform lies within 1e-4 of a cumulative value."""
+    B, S, V, N = 64, 64, 50, 4096
+    g = torch.Generator().manual_seed(12)
+    row = torch.randn(V, generator=g) * 2
+    row[7] = -math.inf
+    x = row.expand(B, S, V).contiguous()
+    u = ((torch.arange(N, dtype=torch.float64) + 0.5) / N).float().reshape(B, S)
+    tokens, mask = synth.make_mask_state(B, S)
+    got = gpu_unmask(x, mask, tokens, gamma=-1.0, temperature=0.5, steps_left=1, uniforms=u)
+    drawn = got["tokens"].reshape(-1)
+    assert np.all(np.diff(drawn) >= 0), "draws must not decrease as u grows"
+    p = scipy.special.softmax(row.double().numpy() / 0.5)
+    counts = np.bincount(drawn, minlength=V)
+    assert counts[7] == 0
+    slack = 1 + 2 * 1e-4 * N
+    assert np.all(np.abs(counts - N * p) <= slack), np.abs(counts - N * p).max()
