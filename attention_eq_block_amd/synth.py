@@ -216,7 +216,7 @@ def random_mask_state(B: int, S: int, p_masked: float, seed: int = 0, device="cp
     return tokens.to(device), mask.to(device)
 
 
-SUB_UNIFORM = 13
+SUB_UNIFORM = 17
 
 
 def make_uniforms(B: int, S: int, seed: int = 0, step: int = 0, device="cpu") -> torch.Tensor:

@@ -84,9 +84,11 @@ def test_sample_strided_rows_many_splits(dtype):
     base = torch.randn(2, 5, 100043, generator=torch.Generator().manual_seed(4)).to(dtype)
     x = base[:, :, 3:100003]
     tokens, mask = synth.make_mask_state(2, 5)
-    for temp, seed in ((1.0, 1), (0.2, 2), (5.0, 3)):
+    # at temperature 5 every confidence is about 1e-5, so the fallback's cut is always within 1e-6:
+    # that case commits every position (one step left) and checks the draws alone
+    for temp, seed, R in ((1.0, 1, 5), (0.2, 2, 5), (5.0, 3, 1)):
         u = synth.make_uniforms(2, 5, seed=seed)
-        check_unmask(x, mask, tokens, gamma=0.5, temperature=temp, steps_left=5, uniforms=u,
+        check_unmask(x, mask, tokens, gamma=0.5, temperature=temp, steps_left=R, uniforms=u,
                      what=f"strided T={temp}", max_fragile_frac=0.5)
 
 
