@@ -74,6 +74,9 @@ class TTError(RuntimeError):
         super().__init__(f"{what}: {STATUS.get(code, code)}")
 
 
+# parameter-struct layouts above match this version of include/twotower_attn.h
+ABI_VERSION = 2
+
 _lib = None
 
 
@@ -87,6 +90,9 @@ def lib():
                 "(or __graft_entry__.build()); there is no fallback implementation")
         L = ctypes.CDLL(LIB_PATH)
         L.tt_abi_version.restype = ctypes.c_int
+        if L.tt_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {L.tt_abi_version()}, these bindings need "
+                               f"{ABI_VERSION}: rebuild it with `python -m attention_eq_block_amd.build`")
         L.tt_status_string.restype = ctypes.c_char_p
         L.tt_status_string.argtypes = [ctypes.c_int]
         L.tt_block_attn_workspace_bytes.restype = c_size

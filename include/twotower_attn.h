@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define TT_ABI_VERSION 1
+#define TT_ABI_VERSION 2  /* 2: tt_conf_unmask_params gained uniforms */
 
 typedef enum tt_status {
     TT_OK = 0,

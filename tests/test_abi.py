@@ -19,7 +19,7 @@ FAKE = 0x1000  # never dereferenced: every call below must fail validation first
 
 def test_library_loads_and_reports_version():
     L = _lib.lib()
-    assert L.tt_abi_version() == 1
+    assert L.tt_abi_version() == 2
 
 
 def test_exports_every_header_function():
