@@ -226,14 +226,15 @@ __device__ __forceinline__ int walk_run(const char* rp, const char* body, int a0
         if (e > 0.f) lastpos = v;
         if (FIND && base + s > r) { e_hit = e; return v; }
     }
-    // chunks in batches of 8 loads in flight; the additions stay in index order in both modes
+    // chunks in batches of NB loads in flight; the additions stay in index order in both modes
+    constexpr int NB = BF16 ? 16 : 8;
     int ch = q0;
-    for (; ch + 7 < q1; ch += 8) {
-        float f[8][8];
+    for (; ch + NB - 1 < q1; ch += NB) {
+        float f[NB][8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) load_chunk<BF16>(body, ch + k, f[k]);
+        for (int k = 0; k < NB; ++k) load_chunk<BF16>(body, ch + k, f[k]);
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
+        for (int k = 0; k < NB; ++k)
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(f[k][j], c, -mc));
@@ -271,25 +272,27 @@ __global__ __launch_bounds__(256) void sample_locate(UArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const long long rows = (long long)a.B * a.S;
     const float c = a.c;
-    __shared__ float sh_m, sh_z, sh_r;
+    __shared__ float sh_m, sh_z, sh_r, sh_u;
     __shared__ int sh_k, sh_am;
     __shared__ float wsum[4];
     __shared__ int wfirst[4], wlast[4];
+    __shared__ Triple tri[64];  // n_vsplit <= 64
+    // the split triples and the uniform arrive together, one load per thread
+    if (tid < a.n_vsplit) tri[tid] = a.part[(long long)tid * rows + row];
+    if (tid == 128) sh_u = a.uniforms[row];
+    __syncthreads();
     if (tid == 0) {
         float m = -INFINITY, z = 0.f;
         int am = INT_MAX;
-        for (int k = 0; k < a.n_vsplit; ++k) {
-            const Triple t = a.part[(long long)k * rows + row];
-            combine(m, am, z, t.m, t.a, t.z, c);
-        }
-        float u = a.uniforms[row];
+        for (int k = 0; k < a.n_vsplit; ++k) combine(m, am, z, tri[k].m, tri[k].a, tri[k].z, c);
+        float u = sh_u;
         u = u > 0.f ? fminf(u, 1.f) : 0.f;  // NaN and negatives count as 0
         const float t = u * z;
         int kk = -1, klast = -1;
         float W = 0.f, r = INFINITY;
         if (m != -INFINITY) {
             for (int k = 0; k < a.n_vsplit; ++k) {
-                const Triple tr = a.part[(long long)k * rows + row];
+                const Triple tr = tri[k];
                 const float wk = tr.m == -INFINITY ? 0.f : tr.z * __builtin_amdgcn_exp2f((tr.m - m) * c);
                 if (wk > 0.f) klast = k;
                 if (kk < 0 && W + wk > t) { kk = k; r = t - W; }
