@@ -458,8 +458,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true", help="run only the counter-reference copy")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (the data-parallel "
-              "sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (the data-parallel "
+              "sharding exists as a design only); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
