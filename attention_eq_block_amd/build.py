@@ -30,8 +30,11 @@ COMMON = [
     # no packed fp32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # MFMA accumulators in VGPRs: the register allocator then keeps operands and
-    # prefetched tiles in AGPRs instead of spilling (attention kernel: 0 spills)
+    # prefetched tiles in AGPRs instead of spilling
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+    # schedule for memory clauses: the attention kernel's spills drop from 48 to 3 registers and its
+    # call time by 1-7% on the loop, long and ragged workloads (A/B in one process)
+    "-mllvm", "-amdgpu-sched-strategy=max-memory-clause",
     "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas",
 ]
 

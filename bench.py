@@ -46,12 +46,17 @@ from attention_eq_block_amd import api, synth  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_loop_hbm_traffic.txt")
 KERNEL_SOURCE = os.path.join(ROOT, "attention_eq_block_amd", "csrc", "attn_bf16.hip")
+BUILD_SCRIPT = os.path.join(ROOT, "attention_eq_block_amd", "build.py")
 COPY_BYTES = 1 << 30
 
 
 def kernel_source_hash():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """Hash of the attention kernel's source and of the build script (its compiler flags)."""
+    h = hashlib.sha256()
+    for path in (KERNEL_SOURCE, BUILD_SCRIPT):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic():
