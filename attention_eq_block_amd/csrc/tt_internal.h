@@ -47,6 +47,10 @@ tt_status launch_kv_append(const tt_kv_append_params& p, hipStream_t s);
 tt_status launch_lse_merge(int P, const float* O_parts, const float* lse_parts, int B, int S, int Hq,
                            int d, void* O_out, int o_dtype, float* lse_out, hipStream_t s);
 
+// sample_locate keeps one total per 64 chunks of a vocabulary split in LDS: with
+// at most 64 splits this bounds a sampled vocabulary at 64 * 4096 * 512 = 2^27.
+constexpr int kSampleMaxIter = 4096;
+
 struct UnmaskPlan {
     int n_vsplit;
     size_t ws_part;  // split triples; the drawn tokens follow when sampling

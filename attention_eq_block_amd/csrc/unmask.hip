@@ -209,62 +209,59 @@ __device__ __forceinline__ void load_chunk(const char* body, int ch, float (&f)[
     }
 }
 
-// One thread's run of a split, in increasing index order: elements [0, head)
-// of the row, chunks [q0, q1) of the body (element a0 + 8 * chunk onwards),
-// then elements [tail0, tail1). Adds e_v = 2^(x_v c - m c) to s one element at a
-// time. With FIND it stops at the first element where base + s > r and returns
-// its index (e_hit = its e_v); it returns -1 otherwise. lastpos is the last
-// index seen with e_v > 0. Both instantiations perform the same additions in
-// the same order, so a run that passes r in the scan also passes it here.
-template <bool BF16, bool FIND>
-__device__ __forceinline__ int walk_run(const char* rp, const char* body, int a0, int head, int q0, int q1,
-                                        int tail0, int tail1, float c, float mc, float base, float r, float& s,
-                                        int& lastpos, float& e_hit) {
-    for (int v = 0; v < head; ++v) {
+// Inclusive sum over the 64 lanes of a wave, in a fixed tree order (the same
+// values give the same result in every call).
+__device__ __forceinline__ float wave_incl_scan(float x, int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+// Weights e_v = 2^(x_v c - m c) of one 8-element chunk summed in index order;
+// lastpos becomes the chunk's last index of nonzero weight.
+template <bool BF16>
+__device__ __forceinline__ float chunk_sum(const char* body, int ch, int v0, float c, float mc, float (&e)[8],
+                                           int& lastpos) {
+    float f[8];
+    load_chunk<BF16>(body, ch, f);
+    float cs = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(f[j], c, -mc));
+        cs += e[j];
+        if (e[j] > 0.f) lastpos = max(lastpos, v0 + j);
+    }
+    return cs;
+}
+
+// Elements [lo, hi) of a row one at a time from base: the first index where the
+// running sum passes r (e_hit its weight), else -1; lastpos and the sum as above.
+template <bool BF16>
+__device__ __forceinline__ int walk_elems(const char* rp, int lo, int hi, float c, float mc, float base, float r,
+                                          float& sum, int& lastpos, float& e_hit) {
+    float x = base;
+    for (int v = lo; v < hi; ++v) {
         const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(elem<BF16>(rp, v), c, -mc));
-        s += e;
-        if (e > 0.f) lastpos = v;
-        if (FIND && base + s > r) { e_hit = e; return v; }
+        x += e;
+        if (e > 0.f) lastpos = max(lastpos, v);
+        if (x > r) { e_hit = e; sum = x; return v; }
     }
-    // chunks in batches of NB loads in flight; the additions stay in index order in both modes
-    constexpr int NB = BF16 ? 16 : 8;
-    int ch = q0;
-    for (; ch + NB - 1 < q1; ch += NB) {
-        float f[NB][8];
-#pragma unroll
-        for (int k = 0; k < NB; ++k) load_chunk<BF16>(body, ch + k, f[k]);
-#pragma unroll
-        for (int k = 0; k < NB; ++k)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(f[k][j], c, -mc));
-                s += e;
-                if (e > 0.f) lastpos = a0 + (ch + k) * 8 + j;
-                if (FIND && base + s > r) { e_hit = e; return a0 + (ch + k) * 8 + j; }
-            }
-    }
-    for (; ch < q1; ++ch) {
-        float f[8];
-        load_chunk<BF16>(body, ch, f);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(f[j], c, -mc));
-            s += e;
-            if (e > 0.f) lastpos = a0 + ch * 8 + j;
-            if (FIND && base + s > r) { e_hit = e; return a0 + ch * 8 + j; }
-        }
-    }
-    for (int v = tail0; v < tail1; ++v) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(elem<BF16>(rp, v), c, -mc));
-        s += e;
-        if (e > 0.f) lastpos = v;
-        if (FIND && base + s > r) { e_hit = e; return v; }
-    }
+    sum = x;
     return -1;
 }
 
 // Inverse transform draw for every masked row (one workgroup of 256 threads
-// per row), after vocab_reduce has written the split triples.
+// per row), after vocab_reduce has written the split triples. The split that
+// holds the crossing is cut into its head (elements before the first aligned
+// chunk, split 0 only), iterations of 64 consecutive chunks (wave i takes
+// iterations i, i + 4, ..., one chunk per lane, so every load is coalesced)
+// and its tail (last split only). The region totals go to LDS; one thread adds
+// them in order and finds the region where the running sum passes the target;
+// that region alone is read again, and inside an iteration the first lane whose
+// scan value passes walks its chunk element by element.
 template <bool BF16>
 __global__ __launch_bounds__(256) void sample_locate(UArgs a) {
     const int row = blockIdx.x;
@@ -272,12 +269,11 @@ __global__ __launch_bounds__(256) void sample_locate(UArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const long long rows = (long long)a.B * a.S;
     const float c = a.c;
-    __shared__ float sh_m, sh_z, sh_r, sh_u;
-    __shared__ int sh_k, sh_am;
-    __shared__ float wsum[4];
-    __shared__ int wfirst[4], wlast[4];
-    __shared__ Triple tri[64];  // n_vsplit <= 64
-    // the split triples and the uniform arrive together, one load per thread
+    __shared__ float sh_m, sh_z, sh_r, sh_u, sh_base;
+    __shared__ int sh_k, sh_am, sh_region;
+    __shared__ int wlast[4];
+    __shared__ Triple tri[64];                   // n_vsplit <= 64
+    __shared__ float tot[kSampleMaxIter + 2];    // head, iterations, tail
     if (tid < a.n_vsplit) tri[tid] = a.part[(long long)tid * rows + row];
     if (tid == 128) sh_u = a.uniforms[row];
     __syncthreads();
@@ -292,8 +288,7 @@ __global__ __launch_bounds__(256) void sample_locate(UArgs a) {
         float W = 0.f, r = INFINITY;
         if (m != -INFINITY) {
             for (int k = 0; k < a.n_vsplit; ++k) {
-                const Triple tr = tri[k];
-                const float wk = tr.m == -INFINITY ? 0.f : tr.z * __builtin_amdgcn_exp2f((tr.m - m) * c);
+                const float wk = tri[k].m == -INFINITY ? 0.f : tri[k].z * __builtin_amdgcn_exp2f((tri[k].m - m) * c);
                 if (wk > 0.f) klast = k;
                 if (kk < 0 && W + wk > t) { kk = k; r = t - W; }
                 W += wk;
@@ -317,53 +312,119 @@ __global__ __launch_bounds__(256) void sample_locate(UArgs a) {
     const int nfull = (a.V - a0) / 8;
     const int per = (nfull + a.n_vsplit - 1) / a.n_vsplit;
     const int c0 = min(nfull, k * per), c1 = min(nfull, c0 + per);
-    const int q = (c1 - c0 + 255) / 256;
-    const int q0 = min(c1, c0 + tid * q), q1 = min(c1, q0 + q);
-    const int head = (k == 0 && tid == 0) ? a0 : 0;
+    const int head = k == 0 ? a0 : 0;
     const int tail0 = a0 + nfull * 8;
-    const int tail1 = (k == a.n_vsplit - 1 && tid == 255) ? a.V : tail0;
+    const int tail1 = k == a.n_vsplit - 1 ? a.V : tail0;
+    const int NI = (c1 - c0 + 63) / 64;  // <= kSampleMaxIter (checked on the host)
     const char* body = rp + a0 * ES;
-    float s = 0.f, e_hit = 0.f;
     int lastpos = -1;
-    walk_run<BF16, false>(rp, body, a0, head, q0, q1, tail0, tail1, c, mc, 0.f, 0.f, s, lastpos, e_hit);
-    // workgroup exclusive scan of the run sums, in thread order
-    float incl = s;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
+    float scratch_sum, e_dummy;
+    if (tid == 0) {
+        walk_elems<BF16>(rp, 0, head, c, mc, 0.f, INFINITY, scratch_sum, lastpos, e_dummy);
+        tot[0] = scratch_sum;
     }
-    float excl = __shfl_up(incl, 1);
-    if (lane == 0) excl = 0.f;
+    if (tid == 64) {
+        walk_elems<BF16>(rp, tail0, tail1, c, mc, 0.f, INFINITY, scratch_sum, lastpos, e_dummy);
+        tot[NI + 1] = scratch_sum;
+    }
+    // pass 1: region totals, NQ iterations of loads in flight per wave (lanes past
+    // the split's end load its last chunk again and count nothing, so every load
+    // is unconditional and they issue together)
+    constexpr int NQ = BF16 ? 16 : 8;
+    for (int G0 = w; G0 < NI; G0 += 4 * NQ) {
+        float f[NQ][8];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) load_chunk<BF16>(body, min(c0 + 64 * (G0 + 4 * q) + lane, c1 - 1), f[q]);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int G = G0 + 4 * q;
+            if (G >= NI) break;
+            const int ch = c0 + 64 * G + lane;
+            float cs = 0.f;
+            if (ch < c1) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(f[q][j], c, -mc));
+                    cs += e;
+                    if (e > 0.f) lastpos = max(lastpos, a0 + ch * 8 + j);
+                }
+            }
+            const float incl = wave_incl_scan(cs, lane);
+            if (lane == 63) tot[1 + G] = incl;
+        }
+    }
     int lp = lastpos;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) lp = max(lp, __shfl_xor(lp, off));
-    if (lane == 63) wsum[w] = incl;
     if (lane == 0) wlast[w] = lp;
     __syncthreads();
-    float wb = 0.f;
-    for (int j = 0; j < w; ++j) wb += wsum[j];
-    const float base = wb + excl;
-    const unsigned long long hit = __ballot(base + s > r);
-    if (lane == 0) wfirst[w] = hit ? w * 64 + __builtin_ctzll(hit) : INT_MAX;
-    __syncthreads();
-    const int first = min(min(wfirst[0], wfirst[1]), min(wfirst[2], wfirst[3]));
-    if (first == INT_MAX) {
-        // u * Z not passed inside the split (u = 1, or rounding): its last element of nonzero weight
-        if (tid == 0) {
-            const int last = max(max(wlast[0], wlast[1]), max(wlast[2], wlast[3]));
-            if (last < 0) {
-                a.drawn[row] = Drawn{sh_am, 1.f / z};
-            } else {
-                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(elem<BF16>(rp, last), c, -mc));
-                a.drawn[row] = Drawn{last, e / z};
-            }
+    if (tid == 0) {
+        float run = 0.f;
+        int region = -1;
+        for (int i = 0; i < NI + 2; ++i) {
+            if (run + tot[i] > r) { region = i; break; }
+            run += tot[i];
         }
-    } else if (tid == first) {
-        float s2 = 0.f;
-        int lp2 = -1;
-        const int v = walk_run<BF16, true>(rp, body, a0, head, q0, q1, tail0, tail1, c, mc, base, r, s2, lp2, e_hit);
-        a.drawn[row] = v >= 0 ? Drawn{v, e_hit / z} : Drawn{sh_am, 1.f / z};
+        sh_region = region;
+        sh_base = run;
+    }
+    __syncthreads();
+    const int region = sh_region;
+    const float base = sh_base;
+    const int last_all = max(max(wlast[0], wlast[1]), max(wlast[2], wlast[3]));
+    auto put = [&](int v, float e) {
+        if (v >= 0) a.drawn[row] = Drawn{v, e / z};
+        else a.drawn[row] = Drawn{sh_am, 1.f / z};
+    };
+    auto weight = [&](int v) { return __builtin_amdgcn_exp2f(__builtin_fmaf(elem<BF16>(rp, v), c, -mc)); };
+    if (region < 0 || region == 0 || region == NI + 1) {
+        if (tid == 0) {
+            int v = -1, lpos = -1;
+            float e = 0.f, sum;
+            if (region == 0) v = walk_elems<BF16>(rp, 0, head, c, mc, base, r, sum, lpos, e);
+            else if (region > 0) v = walk_elems<BF16>(rp, tail0, tail1, c, mc, base, r, sum, lpos, e);
+            if (v < 0) {  // not passed (u = 1, or rounding): the last element of nonzero weight
+                v = region < 0 ? last_all : lpos;
+                if (v < 0) v = last_all;
+                e = v >= 0 ? weight(v) : 0.f;
+            }
+            put(v, e);
+        }
+        return;
+    }
+    const int G = region - 1;
+    if (w != (G & 3)) return;
+    const int ch = c0 + 64 * G + lane;
+    float e[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int lpos = -1;
+    const float cs = ch < c1 ? chunk_sum<BF16>(body, ch, a0 + ch * 8, c, mc, e, lpos) : 0.f;
+    // the same sums as in pass 1, so lane 63 at least passes
+    const float incl = wave_incl_scan(cs, lane);
+    float excl = __shfl_up(incl, 1);
+    if (lane == 0) excl = 0.f;
+    const unsigned long long hit = __ballot(base + incl > r);
+    const int first = hit ? __builtin_ctzll(hit) : 63;
+    int v = -1;
+    float ev = 0.f;
+    if (lane == first) {
+        float x = base + excl;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            x += e[j];
+            if (v < 0 && x > r && e[j] > 0.f) { v = a0 + ch * 8 + j; ev = e[j]; }
+        }
+        if (v < 0 && lpos >= 0) { v = lpos; ev = e[lpos - (a0 + ch * 8)]; }
+    }
+    if (__shfl(v, first) >= 0) {
+        if (lane == first) put(v, ev);
+        return;
+    }
+    // the passing lane's chunk has no weight (a scan rounding): the last weighted lane before it
+    const unsigned long long below = __ballot(cs > 0.f && lane < first);
+    if (below) {
+        if (lane == 63 - __builtin_clzll(below)) put(lpos, e[lpos - (a0 + ch * 8)]);
+    } else if (lane == 0) {
+        put(last_all, last_all >= 0 ? weight(last_all) : 0.f);
     }
 }
 
@@ -461,6 +522,14 @@ __global__ __launch_bounds__(256) void nll_finish(UArgs a, const int* __restrict
 
 }  // namespace
 
+// Iterations of 64 chunks in the largest vocabulary split (an upper bound over
+// the row alignments), which sample_locate's LDS table must hold.
+static long long sample_iterations(const tt_conf_unmask_params& p, const UnmaskPlan& pl) {
+    const long long nfull = (long long)p.V / 8;
+    const long long per = (nfull + pl.n_vsplit - 1) / pl.n_vsplit;
+    return (per + 63) / 64;
+}
+
 UnmaskPlan plan_unmask(const tt_conf_unmask_params& p, int n_cu) {
     UnmaskPlan pl{};
     const long long rows = (long long)p.B * p.S;
@@ -492,6 +561,7 @@ tt_status launch_unmask(const tt_conf_unmask_params& p, const UnmaskPlan& pl, vo
     a.steps_left = p.steps_left;
     a.gamma = p.gamma;
     a.c = 1.44269504088896340736f / p.temperature;
+    if (p.uniforms && sample_iterations(p, pl) > kSampleMaxIter) return TT_ERR_SHAPE;
     a.uniforms = p.uniforms;
     a.drawn = p.uniforms ? reinterpret_cast<Drawn*>(static_cast<char*>(ws) + pl.ws_part) : nullptr;
     const dim3 grid(p.B * p.S, pl.n_vsplit);

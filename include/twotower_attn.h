@@ -209,7 +209,10 @@ tt_status tt_lse_merge(int P, const float* O_parts, const float* lse_parts, int 
  *            clamped to it and NaN counts as 0. The caller owns the generator:
  *            the library draws no random numbers. The cumulative sums are
  *            float32, so a u within about 1e-5 of a cumulative value may select
- *            the neighbouring token.
+ *            the neighbouring token. With uniforms, V <= 2^21 is always
+ *            accepted; larger vocabularies need enough rows that each
+ *            vocabulary split of the launch holds at most 2^21 logits, else
+ *            the call returns TT_ERR_SHAPE before launching anything.
  */
 typedef struct tt_conf_unmask_params {
     int32_t dtype;  /* tt_dtype of logits */
