@@ -335,22 +335,28 @@ __global__ __launch_bounds__(256) void sample_locate(UArgs a) {
         float f[NQ][8];
 #pragma unroll
         for (int q = 0; q < NQ; ++q) load_chunk<BF16>(body, min(c0 + 64 * (G0 + 4 * q) + lane, c1 - 1), f[q]);
+        float cs[NQ], incl[NQ];
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             const int G = G0 + 4 * q;
-            if (G >= NI) break;
             const int ch = c0 + 64 * G + lane;
-            float cs = 0.f;
-            if (ch < c1) {
+            cs[q] = 0.f;
+            if (G < NI && ch < c1) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(f[q][j], c, -mc));
-                    cs += e;
+                    cs[q] += e;
                     if (e > 0.f) lastpos = max(lastpos, a0 + ch * 8 + j);
                 }
             }
-            const float incl = wave_incl_scan(cs, lane);
-            if (lane == 63) tot[1 + G] = incl;
+        }
+        // independent scans, so their shuffles overlap
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) incl[q] = wave_incl_scan(cs[q], lane);
+        if (lane == 63) {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+                if (G0 + 4 * q < NI) tot[1 + G0 + 4 * q] = incl[q];
         }
     }
     int lp = lastpos;
@@ -358,15 +364,31 @@ __global__ __launch_bounds__(256) void sample_locate(UArgs a) {
     for (int off = 32; off > 0; off >>= 1) lp = max(lp, __shfl_xor(lp, off));
     if (lane == 0) wlast[w] = lp;
     __syncthreads();
-    if (tid == 0) {
-        float run = 0.f;
+    // the first region whose total takes the running sum past r: wave 0 scans the
+    // totals 64 at a time; region i starts from base_i = carry + (exclusive scan)
+    if (w == 0) {
+        float carry = 0.f, base_hit = 0.f;
         int region = -1;
-        for (int i = 0; i < NI + 2; ++i) {
-            if (run + tot[i] > r) { region = i; break; }
-            run += tot[i];
+        for (int i0 = 0; i0 < NI + 2; i0 += 64) {
+            const int i = i0 + lane;
+            const float T = i < NI + 2 ? tot[i] : 0.f;
+            const float inc = wave_incl_scan(T, lane);
+            float exc = __shfl_up(inc, 1);
+            if (lane == 0) exc = 0.f;
+            const float bi = carry + exc;
+            const unsigned long long hit = __ballot(i < NI + 2 && bi + T > r);
+            if (hit) {
+                const int l = __builtin_ctzll(hit);
+                region = i0 + l;
+                base_hit = __shfl(bi, l);
+                break;
+            }
+            carry += __shfl(inc, 63);
         }
-        sh_region = region;
-        sh_base = run;
+        if (lane == 0) {
+            sh_region = region;
+            sh_base = base_hit;
+        }
     }
     __syncthreads();
     const int region = sh_region;
