@@ -221,3 +221,22 @@ def test_nll_needs_workspace_and_zero_batch_noop():
     assert L.tt_masked_nll(ctypes.byref(nll_ok()), None, nb, None) == 5
     assert L.tt_masked_nll(ctypes.byref(nll_ok(B=0, logits=None)), None, 0, None) == 0
     assert L.tt_masked_nll(None, None, 0, None) == 1
+
+
+def test_unmask_sampling_workspace_holds_the_draws():
+    """With uniforms the workspace also holds one (token, confidence) pair of 8 bytes per position."""
+    L = _lib.lib()
+    g = L.tt_conf_unmask_workspace_bytes(ctypes.byref(unmask_ok()))
+    s = L.tt_conf_unmask_workspace_bytes(ctypes.byref(unmask_ok(uniforms=FAKE)))
+    assert s == g + 4 * 16 * 8
+
+
+def test_unmask_sampling_vocabulary_bound():
+    """With uniforms a vocabulary split may hold at most 2^21 logits. 4096 rows use one split, so
+    V = 2^21 + 512 is refused with TT_ERR_SHAPE, before any launch (the pointers here are fake)."""
+    L = _lib.lib()
+    big = (1 << 21) + 512
+    p = unmask_ok(B=256, S=16, V=big, logits_stride_row=big, uniforms=FAKE)
+    nb = L.tt_conf_unmask_workspace_bytes(ctypes.byref(p))
+    assert nb > 0
+    assert L.tt_conf_unmask(ctypes.byref(p), FAKE, nb, None) == 2
