@@ -102,7 +102,7 @@ class Layer:
             raise RuntimeError(f"tt_block_attn failed: {api.status_string(rc)}")
 
 
-def cpu_baseline_loop(layers, logits, case, ucase, budget_s=12.0):
+def cpu_baseline_loop(layers, logits, case, ucase, budget_s=12.0, uniforms=None):
     """The float64 oracle on whole sequences of the same workload (one layer's attention
     per sequence plus one unmask step), scaled to tokens/s per attention layer."""
     import oracle
@@ -128,7 +128,7 @@ def cpu_baseline_loop(layers, logits, case, ucase, budget_s=12.0):
         x = logits[0][:n].cpu()
         tok, mk = synth.make_mask_state(n, S)
         oracle.conf_unmask(x, mk, tok, gamma=oracle.f32(ucase.gamma), temperature=oracle.f32(ucase.temperature),
-                           steps_left=synth.LOOP_STEPS)
+                           steps_left=synth.LOOP_STEPS, uniforms=None if uniforms is None else uniforms[:n].cpu())
         t2 = time.perf_counter()
         return t1 - t0, t2 - t1
 
@@ -160,8 +160,10 @@ def run_loop(args):
     mask = torch.empty((B, S), dtype=torch.uint8, device="cuda")
     nmask = torch.empty((B,), dtype=torch.int32, device="cuda")
     nm_host = torch.empty((B,), dtype=torch.int32, pin_memory=True)
+    # --sample: each step draws its tokens from softmax(logits / temperature) with fresh uniforms
+    unis = [synth.make_uniforms(B, S, seed=0, step=r, device="cuda") for r in range(1, T + 1)] if args.sample else None
     up = api.unmask_params(logits[0], mask, tokens, gamma=ucase.gamma, temperature=ucase.temperature,
-                           steps_left=T, num_masked=nmask)
+                           steps_left=T, num_masked=nmask, uniforms=unis[0] if unis else None)
     uws = torch.empty(max(16, api.conf_unmask_workspace_bytes(up)), dtype=torch.uint8, device="cuda")
     lib = api.lib()
     stream = torch.cuda.current_stream()
@@ -181,6 +183,8 @@ def run_loop(args):
                 ev[r - 1][1].record(stream)
             up.logits = logits[r - 1].data_ptr()
             up.steps_left = T - r + 1
+            if unis:
+                up.uniforms = unis[r - 1].data_ptr()
             rc = lib.tt_conf_unmask(up, uws.data_ptr(), uws.numel(), sh)
             if rc:
                 raise RuntimeError(f"tt_conf_unmask failed: {api.status_string(rc)}")
@@ -220,7 +224,9 @@ def run_loop(args):
         "warmup": args.warmup, "ms_per_step": ms_per_block, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "full-block denoise loop (Algorithm 2): batch 32, S=16, T=16, 6 attention layers, "
-                               "prefix 8192, 32 q / 2 kv heads, head_dim 128, V=131072, gamma 0.8, temperature 0.1",
+                               "prefix 8192, 32 q / 2 kv heads, head_dim 128, V=131072, "
+                               f"gamma {args.gamma:g}, temperature {args.temperature:g}"
+                               + (", stochastic draws" if args.sample else ""),
                    "global_batch": B, "seq_len": case.ctx_lens[0] + S, "parallelism": "none",
                    "denoise_steps_per_block": steps_per_block, "blocks_per_s": B * args.steps / wall,
                    "attn_call_us": call_ms * 1e3, "attn_call_tokens_per_s": B * S / (call_ms * 1e-3)},
@@ -231,7 +237,7 @@ def run_loop(args):
     }
     if not args.no_cpu:
         log("[bench] cpu baseline (oracle)")
-        res["cpu_baseline"] = cpu_baseline_loop(layers, logits, case, ucase)
+        res["cpu_baseline"] = cpu_baseline_loop(layers, logits, case, ucase, uniforms=unis[0] if unis else None)
     return res
 
 
@@ -459,6 +465,8 @@ def main():
     ap.add_argument("--workload", default="loop", choices=["loop", "single", "ragged", "long", "append", "nll", "sample"])
     ap.add_argument("--gamma", type=float, default=0.8)
     ap.add_argument("--temperature", type=float, default=0.1)
+    ap.add_argument("--sample", action="store_true",
+                    help="loop workload: draw tokens at the temperature (caller uniforms) instead of the argmax")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true", help="run only the counter-reference copy")
     args = ap.parse_args()
