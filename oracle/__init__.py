@@ -44,8 +44,8 @@ def load(path: Optional[str] = None):
 
 def _bind(lib):
     lib.oracle_block_attn.restype = _I
-    lib.oracle_block_attn.argtypes = [_I, _I, _I, _I, _I, _I, ctypes.c_double, _P, _P, _P, _I, _P, _I,
-                                      _P, _P, _P, _I, _P, _P, _P]
+    lib.oracle_block_attn.argtypes = [_I, _I, _I, _I, _I, _I, ctypes.c_double, _P, _P, _P, _I, _I, _P, _I,
+                                      _P, _I, _P, _P, _I, _P, _P, _P]
     lib.oracle_lse_merge.restype = _I
     lib.oracle_lse_merge.argtypes = [_I, _I, _I, _P, _P, _P, _P]
     lib.oracle_conf_unmask.restype = _I
@@ -112,11 +112,15 @@ def all_rows(B: int, Hq: int, S: int) -> np.ndarray:
 
 
 def block_attn(Q, Kc, Vc, page_table, ctx_len, Kd=None, Vd=None, *, page_size: int,
-               scale: float, rows=None):
+               scale: float, rows=None, max_ctx_len: Optional[int] = None):
     """Eq. (1) for the selected (b, h, s) rows (all rows when ``rows`` is None).
 
     Returns (O, LSE) as float64 numpy arrays: with ``rows=None`` they have the
     shapes [B][S][Hq][D] and [B][Hq][S]; otherwise [n][D] and [n].
+
+    Out-of-range data reads as the library defines it: a prefix length clamped into
+    [0, min(max_ctx_len, max_pages * page_size)] (no max_ctx_len: the table's
+    capacity), a page id clamped into [0, num_pages).
     """
     B, S, Hq, D = Q.shape
     Hkv = Kc.shape[1]
@@ -131,13 +135,15 @@ def block_attn(Q, Kc, Vc, page_table, ctx_len, Kd=None, Vd=None, *, page_size: i
         raise TypeError("Q and the cache must share a dtype")
     pt = _i32(page_table).reshape(B, -1)
     cl = _i32(ctx_len)
+    cap = pt.shape[1] * int(page_size)
+    len_cap = cap if max_ctx_len is None else min(int(max_ctx_len), cap)
     full = rows is None
     r = all_rows(B, Hq, S) if full else _i32(rows).reshape(-1, 3)
     n = r.shape[0]
     O = np.zeros((n, D), np.float64)
     L = np.zeros((n,), np.float64)
-    rc = load().oracle_block_attn(dt, B, S, Hq, Hkv, D, float(scale), qp, kp, vp, int(page_size),
-                                  pt.ctypes.data, pt.shape[1], cl.ctypes.data, kdp, vdp, n,
+    rc = load().oracle_block_attn(dt, B, S, Hq, Hkv, D, float(scale), qp, kp, vp, int(page_size), int(Kc.shape[0]),
+                                  pt.ctypes.data, pt.shape[1], cl.ctypes.data, len_cap, kdp, vdp, n,
                                   r.ctypes.data, O.ctypes.data, L.ctypes.data)
     if rc != 0:
         raise ValueError("oracle_block_attn rejected its arguments")

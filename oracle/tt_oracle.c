@@ -65,13 +65,19 @@ int oracle_num_threads(void) {
  *   O          [n_rows][D] double, LSE [n_rows] double (natural log)
  * Query head h reads KV head h / (Hq/Hkv). An empty key set gives O=0 and
  * LSE=-inf. Returns 0, or -1 on bad arguments.
+ *
+ * Out-of-range device data (not the paper's; the library's contract, so that
+ * corrupt data never makes it read outside its arrays): a prefix length is
+ * taken clamped into [0, len_cap] (len_cap = min(max_ctx_len, max_pages *
+ * page_size)), and a page id clamped into [0, num_pages).
  */
 int oracle_block_attn(int dtype, int B, int S, int Hq, int Hkv, int D, double scale,
-                      const void* Q, const void* Kc, const void* Vc, int page_size,
-                      const int32_t* page_table, int max_pages, const int32_t* ctx_len,
+                      const void* Q, const void* Kc, const void* Vc, int page_size, int num_pages,
+                      const int32_t* page_table, int max_pages, const int32_t* ctx_len, int len_cap,
                       const void* Kd, const void* Vd, int n_rows, const int32_t* rows,
                       double* O, double* LSE) {
-    if (Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || page_size <= 0) return -1;
+    if (Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || page_size <= 0 || num_pages <= 0 || len_cap < 0) return -1;
+    if ((long long)len_cap > (long long)max_pages * page_size) return -1;
     const int G = Hq / Hkv;
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
@@ -79,7 +85,9 @@ int oracle_block_attn(int dtype, int B, int S, int Hq, int Hkv, int D, double sc
         const int b = rows[3 * r], h = rows[3 * r + 1], s = rows[3 * r + 2];
         if (b < 0 || b >= B || h < 0 || h >= Hq || s < 0 || s >= S) { bad = 1; continue; }
         const int g = h / G;
-        const int L = ctx_len[b];
+        int L = ctx_len[b];
+        if (L < 0) L = 0;
+        if (L > len_cap) L = len_cap;
         const int n = L + (Kd ? S : 0);
         double* o = O + (size_t)r * D;
         for (int k = 0; k < D; ++k) o[k] = 0.0;
@@ -93,7 +101,9 @@ int oracle_block_attn(int dtype, int B, int S, int Hq, int Hkv, int D, double sc
         for (int j = 0; j < n; ++j) {
             int src;
             if (j < L) {
-                const int page = page_table[(size_t)b * max_pages + j / page_size];
+                int page = page_table[(size_t)b * max_pages + j / page_size];
+                if (page < 0) page = 0;
+                if (page >= num_pages) page = num_pages - 1;
                 off[j] = (((size_t)page * Hkv + g) * page_size + j % page_size) * D;
                 src = 0;
             } else {

@@ -308,6 +308,30 @@ def pin_attn_dominant_key():
     close(L[0, 0, 0], 60.0 + math.log1p(20 * math.exp(-60)), 1e-12, "dominant key LSE")
 
 
+def pin_attn_out_of_range_data():
+    """Device data outside the contract reads as its clamp into range (the library's stated
+    behaviour, not the paper's): a negative prefix length as 0, one above max_ctx_len as max_ctx_len,
+    a page id below 0 as page 0 and one past the pool as the last page. Brute force over inputs
+    clamped here with torch.clamp agrees with the oracle given the raw ones."""
+    inp = small_case(B=4, S=3, Hq=4, Hkv=2, D=8, ctx=(37, 21, 40, 5), spare_pages=2)
+    num_pages = inp["Kc"].shape[0]
+    max_ctx = 40
+    cl = torch.tensor([-5, 21, 60, 5], dtype=torch.int32)
+    pt = inp["page_table"].clone()
+    pt[1, 0] = -3
+    pt[2, 1] = num_pages + 7
+    raw = dict(inp, ctx_len=cl, page_table=pt)
+    fixed = dict(inp, ctx_len=cl.clamp(0, max_ctx), page_table=pt.clamp(0, num_pages - 1))
+    B, S, Hq, _ = inp["Q"].shape
+    rows = oracle.all_rows(B, Hq, S)
+    O, L = oracle.block_attn(raw["Q"], raw["Kc"], raw["Vc"], raw["page_table"], raw["ctx_len"], raw["Kd"],
+                             raw["Vd"], page_size=raw["page_size"], scale=raw["scale"], rows=rows,
+                             max_ctx_len=max_ctx)
+    Ob, Lb = brute_attn(fixed, rows.tolist())
+    close(O, Ob, 1e-12, "clamped data O")
+    close(L, Lb, 1e-12, "clamped data LSE")
+
+
 def pin_attn_golden():
     """Hand-worked values (tests/golden/hand_cases.json, attention)."""
     cases = json.load(open(GOLDEN))["attn"]

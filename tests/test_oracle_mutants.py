@@ -21,8 +21,12 @@ MUTANTS = [
     ("drop in-block keys", "const int n = L + (Kd ? S : 0);", "const int n = L;"),
     ("wrong GQA head map", "const int g = h / G;", "const int g = h % Hkv;"),
     ("scale dropped", "sc[j] = scale * dot;", "sc[j] = dot;"),
-    ("page table ignored", "const int page = page_table[(size_t)b * max_pages + j / page_size];",
-     "const int page = b * max_pages + j / page_size;"),
+    ("page table ignored", "int page = page_table[(size_t)b * max_pages + j / page_size];",
+     "int page = b * max_pages + j / page_size;"),
+    ("upper length clamp dropped", "if (L > len_cap) L = len_cap;", ""),
+    ("page id above the pool clamped to page 0", "if (page >= num_pages) page = num_pages - 1;",
+     "if (page >= num_pages) page = 0;"),
+    ("negative page id clamped to the last page", "if (page < 0) page = 0;", "if (page < 0) page = num_pages - 1;"),
     ("slot off by one", "* page_size + j % page_size) * D;", "* page_size + (j + 1) % page_size) * D;"),
     ("Q layout transposed", "const size_t qoff = (((size_t)b * S + s) * Hq + h) * D;",
      "const size_t qoff = (((size_t)b * Hq + h) * S + s) * D;"),
