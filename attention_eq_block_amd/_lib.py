@@ -33,7 +33,7 @@ class BlockAttnParams(ctypes.Structure):
         ("Kden", c_ptr), ("Vden", c_ptr),
         ("den_stride_b", c_i64), ("den_stride_s", c_i64), ("den_stride_h", c_i64),
         ("O", c_ptr), ("o_stride_b", c_i64), ("o_stride_s", c_i64), ("o_stride_h", c_i64),
-        ("LSE", c_ptr),
+        ("LSE", c_ptr), ("debug_flags", c_ptr),
     ]
 
 
@@ -75,7 +75,7 @@ class TTError(RuntimeError):
 
 
 # parameter-struct layouts above match this version of include/twotower_attn.h
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _lib = None
 

@@ -63,18 +63,51 @@ def _ws(nbytes: int, device, workspace: Optional[torch.Tensor]) -> Optional[torc
 
 def attn_params(Q, Kc, Vc, page_table, ctx_len, Kd=None, Vd=None, *, page_size: int, max_ctx_len: int,
                 scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-                lse: Optional[torch.Tensor] = None, o_dtype=None) -> BlockAttnParams:
-    """Build the parameter struct for ``tt_block_attn`` (allocating ``out``/``lse`` if absent)."""
+                lse: Optional[torch.Tensor] = None, o_dtype=None,
+                debug_flags: Optional[torch.Tensor] = None) -> BlockAttnParams:
+    """Build the parameter struct for ``tt_block_attn`` (allocating ``out``/``lse`` if absent).
+
+    Shapes, dtypes and layouts are checked here, before anything reaches the library, so that a
+    mismatched tensor raises ValueError instead of making a kernel read out of bounds.
+    ``debug_flags``: a one-element int32 tensor that turns on the library's device-side data
+    checks (TT_DEBUG_* bits are ORed into it).
+    """
+    if Q.dim() != 4:
+        raise ValueError("Q must be [B][S][Hq][head_dim]")
     B, S, Hq, D = Q.shape
     if Q.stride(3) != 1:
         raise ValueError("Q's head_dim must be contiguous")
     Hkv = Kc.shape[1] if Kc is not None else (Kd.shape[2] if Kd is not None else Hq)
+    if Kc is not None:
+        if Vc is None or Kc.dim() != 4 or tuple(Vc.shape) != tuple(Kc.shape):
+            raise ValueError("Kc and Vc must both be [num_pages][Hkv][page_size][head_dim]")
+        if Kc.shape[3] != D:
+            raise ValueError(f"the cache's head_dim {Kc.shape[3]} differs from Q's {D}")
+        if Kc.dtype != Q.dtype or Vc.dtype != Q.dtype:
+            raise TypeError("the cache must have Q's dtype")
+    if (Kd is None) != (Vd is None):
+        raise ValueError("Kd and Vd go together")
+    if Kd is not None:
+        if tuple(Kd.shape) != (B, S, Hkv, D) or tuple(Vd.shape) != (B, S, Hkv, D):
+            raise ValueError(f"Kd and Vd must be [B][S][Hkv][head_dim] = {(B, S, Hkv, D)}")
+        if Kd.dtype != Q.dtype or Vd.dtype != Q.dtype:
+            raise TypeError("Kd and Vd must have Q's dtype")
+    if ctx_len is not None and tuple(ctx_len.shape) != (B,):
+        raise ValueError("ctx_len must be [B]")
+    if page_table is not None and (page_table.dim() != 2 or page_table.shape[0] < B):
+        raise ValueError("page_table must be [B][max_pages]")
+    if debug_flags is not None and (debug_flags.dtype != torch.int32 or debug_flags.numel() < 1):
+        raise ValueError("debug_flags must be an int32 tensor")
     if o_dtype is None:
         o_dtype = Q.dtype
     if out is None:
         out = torch.empty((B, S, Hq, D), dtype=o_dtype, device=Q.device)
+    elif tuple(out.shape) != (B, S, Hq, D) or out.stride(3) != 1:
+        raise ValueError("out must be [B][S][Hq][head_dim] with head_dim contiguous")
     if lse is None:
         lse = torch.empty((B, Hq, S), dtype=torch.float32, device=Q.device)
+    elif lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, S) or not lse.is_contiguous():
+        raise ValueError("lse must be dense float32 [B][Hq][S]")
     p = BlockAttnParams()
     p.dtype = _code(Q)
     p.o_dtype = _code(out)
@@ -108,6 +141,7 @@ def attn_params(Q, Kc, Vc, page_table, ctx_len, Kd=None, Vd=None, *, page_size: 
     p.O = _ptr(out)
     p.o_stride_b, p.o_stride_s, p.o_stride_h = out.stride(0), out.stride(1), out.stride(2)
     p.LSE = _ptr(lse)
+    p.debug_flags = _ptr(debug_flags)
     p._keep = (out, lse)  # keep outputs alive with the struct
     return p
 
@@ -119,18 +153,18 @@ def block_attn_workspace_bytes(p: BlockAttnParams) -> int:
 def block_attn(Q, Kc, Vc, page_table, ctx_len, Kd=None, Vd=None, *, page_size: int = 16,
                max_ctx_len: Optional[int] = None, scale: Optional[float] = None,
                out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, o_dtype=None,
-               workspace: Optional[torch.Tensor] = None):
+               workspace: Optional[torch.Tensor] = None, debug_flags: Optional[torch.Tensor] = None):
     """Eq. (1) for one attention layer: returns (O [B][S][Hq][D], LSE [B][Hq][S] float32).
 
     Q [B][S][Hq][D]; Kc, Vc [num_pages][Hkv][page_size][D]; page_table [B][max_pages] int32;
     ctx_len [B] int32; Kd, Vd [B][S][Hkv][D] or None (prefix-only partial). ``max_ctx_len``
     is the host-side bound of ctx_len (read back from the device when omitted).
     """
-    _need_cuda(Q, Kc, Vc, page_table, ctx_len, Kd, Vd, out, lse, workspace)
+    _need_cuda(Q, Kc, Vc, page_table, ctx_len, Kd, Vd, out, lse, workspace, debug_flags)
     if max_ctx_len is None:
         max_ctx_len = int(ctx_len.max().item()) if ctx_len is not None and ctx_len.numel() else 0
     p = attn_params(Q, Kc, Vc, page_table, ctx_len, Kd, Vd, page_size=page_size, max_ctx_len=max_ctx_len,
-                    scale=scale, out=out, lse=lse, o_dtype=o_dtype)
+                    scale=scale, out=out, lse=lse, o_dtype=o_dtype, debug_flags=debug_flags)
     out, lse = p._keep
     ws = _ws(block_attn_workspace_bytes(p), Q.device, workspace)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
@@ -171,6 +205,15 @@ def unmask_params(logits, mask_in, tokens, *, gamma: float, temperature: float, 
     if uniforms is not None and (uniforms.dtype != torch.float32 or not uniforms.is_contiguous()
                                  or tuple(uniforms.shape) != (B, S)):
         raise ValueError("uniforms must be dense float32 [B][S]")
+    if mask_out is not None and (mask_out.dtype != torch.uint8 or not mask_out.is_contiguous()
+                                 or tuple(mask_out.shape) != (B, S)):
+        raise ValueError("mask_out must be dense uint8 [B][S]")
+    if conf is not None and (conf.dtype != torch.float32 or not conf.is_contiguous()
+                             or tuple(conf.shape) != (B, S)):
+        raise ValueError("conf must be dense float32 [B][S]")
+    if num_masked is not None and (num_masked.dtype != torch.int32 or not num_masked.is_contiguous()
+                                   or tuple(num_masked.shape) != (B,)):
+        raise ValueError("num_masked must be dense int32 [B]")
     p = ConfUnmaskParams()
     p.dtype = _code(logits)
     p.B, p.S, p.V = B, S, V

@@ -75,6 +75,14 @@ tt_status validate_attn(const tt_block_attn_params* p) {
             !stride_ok(p->den_stride_h, p->dtype))
             return TT_ERR_UNSUPPORTED;
     }
+    // offsets inside one sequence are 32-bit byte offsets in the kernels
+    const int64_t lim = (int64_t)1 << 30;
+    if ((int64_t)(p->S - 1) * p->q_stride_s + (int64_t)(p->Hq - 1) * p->q_stride_h + p->head_dim >= lim ||
+        (int64_t)(p->S - 1) * p->o_stride_s + (int64_t)(p->Hq - 1) * p->o_stride_h + p->head_dim >= lim)
+        return TT_ERR_UNSUPPORTED;
+    if (p->Kden &&
+        (int64_t)(p->S - 1) * p->den_stride_s + (int64_t)(p->Hkv - 1) * p->den_stride_h + p->head_dim >= lim)
+        return TT_ERR_UNSUPPORTED;
     // the bf16 path counts tiles (and the piece-start charge) in 32-bit integers
     const int64_t G = p->Hq / p->Hkv;
     const int64_t n_rb = (p->S * G + tt::kRows - 1) / tt::kRows;
@@ -92,6 +100,8 @@ tt_status validate_unmask(const tt_conf_unmask_params* p) {
     if (p->steps_left < 1) return TT_ERR_ARG;
     if ((int64_t)p->B * p->S >= (int64_t)1 << 31) return TT_ERR_SHAPE;
     if (p->B == 0) return TT_OK;
+    // the stochastic draw re-reads one vocabulary split per row through a bounded LDS table
+    if (p->uniforms && !tt::unmask_sample_fits(*p, tt::plan_unmask(*p, device_cu_count()))) return TT_ERR_SHAPE;
     if (!p->logits || !p->mask_in || !p->mask_out || !p->tokens) return TT_ERR_NULL;
     if ((reinterpret_cast<uintptr_t>(p->logits) % esize(p->dtype)) != 0) return TT_ERR_UNSUPPORTED;
     return TT_OK;

@@ -112,6 +112,7 @@ struct Args {
     int B, S, Hq, Hkv, G, n_rb, has_den, n_seg;
     int pe;  // extra units counted at the start of every pair (its piece-start cost)
     float c_log2;  // softmax_scale * log2(e)
+    int* dbg;  // debug mode: TT_DEBUG_* bits of the out-of-range data read, or null
 };
 
 typedef __attribute__((address_space(4))) const int const_int;
@@ -432,6 +433,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
     const int per_xcd = a.n_seg / 8;
     const int seg = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
 
+    if (TT_UNLIKELY(a.dbg != nullptr) && ctx_len && blockIdx.x == 0 && wave == 0) {
+        bool bad = false;
+        for (int b = lane; b < a.B; b += 64) bad |= ctx_len[b] < 0 || ctx_len[b] > a.Lmax;
+        if (bad) atomicOr(a.dbg, TT_DEBUG_CTX_LEN);
+    }
     int n, b0, pl0, t0;  // tiles of this segment, from tile t0 of pair pl0 of sequence b0
     scan_segment(a, ctx_len, seg, n, b0, pl0, t0, seg == 0 && wave == 0 ? a.units_before : nullptr);
     n = __builtin_amdgcn_readfirstlane(n);
@@ -532,6 +538,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
             page_batch(cl, ul, 64, pbuf ^ 1);    // the batch after next, into the one used up
         }
         const int page = __builtin_amdgcn_readlane(pgl, ul - pg_base);
+        if (TT_UNLIKELY(a.dbg != nullptr) && is_prefix(cl, a) && (page < 0 || page >= a.num_pages) && lane == 0)
+            atomicOr(a.dbg, TT_DEBUG_PAGE_ID);
         load_tile<D, P2>(r, cl, page, src_c, src_d, a, wq, lane, loff);
         if (ul + 1 < n) {
             advance(cl, a, ctx_len);
@@ -1050,6 +1058,7 @@ tt_status launch_attn_bf16(const tt_block_attn_params& p, const AttnPlan& pl, vo
     a.n_seg = pl.n_seg;
     a.pe = kPieceCost;
     a.c_log2 = p.softmax_scale * 1.44269504088896340736f;
+    a.dbg = p.debug_flags;
     a.page_shift = -1;
     if (p.page_size > 0 && (p.page_size & (p.page_size - 1)) == 0) {
         a.page_shift = 0;

@@ -22,6 +22,7 @@ struct F32Args {
     float* O;
     long long osb, oss, osh;
     float* LSE;
+    int* dbg;  // debug mode: TT_DEBUG_* bits of the out-of-range data read, or null
     int B, S, Hq, Hkv, G;
     float scale;
 };
@@ -44,6 +45,10 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(F32Args a) {
     const int b = (int)(row / ((long long)a.Hq * a.S));
     const int g = h / a.G;
     const int L = a.ctx_len ? clamp_len(a.ctx_len[b], a.Lmax) : 0;
+    if (a.dbg && a.ctx_len && lane == 0 && s == 0 && h == 0) {
+        const int raw = a.ctx_len[b];
+        if (raw < 0 || raw > a.Lmax) atomicOr(a.dbg, TT_DEBUG_CTX_LEN);
+    }
     const int n = L + (a.Kd ? a.S : 0);
 
     float q[E], o[E];
@@ -54,11 +59,14 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(F32Args a) {
     for (int j = 0; j < n; ++j) {
         const float* kp;
         const float* vp;
-        bool ok = true;
         if (j < L) {
-            const int page = a.page_table[(long long)b * a.max_pages + j / a.page_size];
-            ok = page >= 0 && page < a.num_pages;
-            const long long off = (((long long)(ok ? page : 0) * a.Hkv + g) * a.page_size + j % a.page_size) * D;
+            // a page id outside the pool is clamped into it (wrong data, no fault)
+            int page = a.page_table[(long long)b * a.max_pages + j / a.page_size];
+            if (page < 0 || page >= a.num_pages) {
+                if (a.dbg && lane == 0) atomicOr(a.dbg, TT_DEBUG_PAGE_ID);
+                page = min(max(page, 0), a.num_pages - 1);
+            }
+            const long long off = (((long long)page * a.Hkv + g) * a.page_size + j % a.page_size) * D;
             kp = a.Kc + off;
             vp = a.Vc + off;
         } else {
@@ -69,8 +77,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(F32Args a) {
         float k[E], v[E];
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            k[e] = ok ? kp[lane * E + e] : 0.f;
-            v[e] = ok ? vp[lane * E + e] : 0.f;
+            k[e] = kp[lane * E + e];
+            v[e] = vp[lane * E + e];
         }
         float part = 0.f;
 #pragma unroll
@@ -110,6 +118,7 @@ tt_status launch_attn_f32(const tt_block_attn_params& p, hipStream_t s) {
     a.O = static_cast<float*>(p.O);
     a.osb = p.o_stride_b; a.oss = p.o_stride_s; a.osh = p.o_stride_h;
     a.LSE = p.LSE;
+    a.dbg = p.debug_flags;
     a.B = p.B; a.S = p.S; a.Hq = p.Hq; a.Hkv = p.Hkv; a.G = p.Hq / p.Hkv;
     a.scale = p.softmax_scale;
     const long long rows = (long long)p.B * p.S * p.Hq;

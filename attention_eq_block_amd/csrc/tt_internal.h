@@ -57,6 +57,8 @@ struct UnmaskPlan {
     size_t ws_total;
 };
 UnmaskPlan plan_unmask(const tt_conf_unmask_params& p, int n_cu);
+// with uniforms: the largest vocabulary split fits sample_locate's table
+bool unmask_sample_fits(const tt_conf_unmask_params& p, const UnmaskPlan& plan);
 UnmaskPlan plan_nll(const tt_masked_nll_params& p, int n_cu);
 tt_status launch_unmask(const tt_conf_unmask_params& p, const UnmaskPlan& plan, void* ws,
                         hipStream_t s);

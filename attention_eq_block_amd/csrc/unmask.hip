@@ -552,6 +552,10 @@ static long long sample_iterations(const tt_conf_unmask_params& p, const UnmaskP
     return (per + 63) / 64;
 }
 
+bool unmask_sample_fits(const tt_conf_unmask_params& p, const UnmaskPlan& pl) {
+    return sample_iterations(p, pl) <= kSampleMaxIter;
+}
+
 UnmaskPlan plan_unmask(const tt_conf_unmask_params& p, int n_cu) {
     UnmaskPlan pl{};
     const long long rows = (long long)p.B * p.S;
@@ -583,7 +587,7 @@ tt_status launch_unmask(const tt_conf_unmask_params& p, const UnmaskPlan& pl, vo
     a.steps_left = p.steps_left;
     a.gamma = p.gamma;
     a.c = 1.44269504088896340736f / p.temperature;
-    if (p.uniforms && sample_iterations(p, pl) > kSampleMaxIter) return TT_ERR_SHAPE;
+    if (p.uniforms && !unmask_sample_fits(p, pl)) return TT_ERR_SHAPE;  // also refused in validation
     a.uniforms = p.uniforms;
     a.drawn = p.uniforms ? reinterpret_cast<Drawn*>(static_cast<char*>(ws) + pl.ws_part) : nullptr;
     const dim3 grid(p.B * p.S, pl.n_vsplit);

@@ -50,7 +50,11 @@
 extern "C" {
 #endif
 
-#define TT_ABI_VERSION 2  /* 2: tt_conf_unmask_params gained uniforms */
+#define TT_ABI_VERSION 3  /* 2: tt_conf_unmask_params gained uniforms; 3: tt_block_attn_params gained debug_flags */
+
+/* Bits tt_block_attn ORs into *debug_flags in debug mode (see tt_block_attn_params). */
+#define TT_DEBUG_CTX_LEN 1  /* a ctx_len[b] below 0 or above max_ctx_len was read */
+#define TT_DEBUG_PAGE_ID 2  /* a page id outside [0, num_pages) was read for a prefix token */
 
 typedef enum tt_status {
     TT_OK = 0,
@@ -114,8 +118,17 @@ const char* tt_status_string(tt_status status);
  * Supported: dtype TT_BF16 (MFMA path, float32 accumulation) or TT_F32
  * (float32 path); head_dim 64 or 128; 1 <= S <= 64; Hq % Hkv == 0;
  * page_size a positive multiple of 16; softmax_scale finite and > 0; every
- * element stride below 2^31 and B*max_pages below 2^30 (TT_ERR_UNSUPPORTED
- * otherwise).
+ * element stride below 2^31, B*max_pages below 2^30, and the largest element
+ * offset inside one sequence of Q, O and Kden/Vden ((S-1)*stride_s +
+ * (H-1)*stride_h + head_dim) below 2^30 (TT_ERR_UNSUPPORTED otherwise).
+ *
+ * Debug mode: when debug_flags is not NULL the kernels also check the device
+ * data they read and OR TT_DEBUG_CTX_LEN (when max_ctx_len > 0: a ctx_len[b]
+ * outside [0, max_ctx_len]) and TT_DEBUG_PAGE_ID (a page id outside
+ * [0, num_pages) for a prefix token) into *debug_flags, a device int32 that
+ * the caller zeroes beforehand and reads after the stream reaches the call.
+ * The outputs are those of the clamped data either way. With debug_flags NULL
+ * nothing is checked.
  */
 typedef struct tt_block_attn_params {
     int32_t dtype;        /* tt_dtype of Q and K/V */
@@ -142,6 +155,7 @@ typedef struct tt_block_attn_params {
     void* O;
     int64_t o_stride_b, o_stride_s, o_stride_h;
     float* LSE;
+    int32_t* debug_flags; /* NULL, or a device int32 that enables the debug-mode checks */
 } tt_block_attn_params;
 
 /* Workspace bytes tt_block_attn needs for these parameters (0 if none). The

@@ -39,20 +39,21 @@ def to_dev(inp, device="cuda"):
     return out
 
 
-def gpu_attn(inp, *, max_ctx_len=None, o_dtype=None, out=None, lse=None):
+def gpu_attn(inp, *, max_ctx_len=None, o_dtype=None, out=None, lse=None, debug_flags=None):
     d = to_dev(inp)
     if max_ctx_len is None:
         max_ctx_len = int(inp["ctx_len"].max()) if inp["ctx_len"].numel() else 0
     O, L = api.block_attn(d["Q"], d["Kc"], d["Vc"], d["page_table"], d["ctx_len"], d.get("Kd"), d.get("Vd"),
                           page_size=inp["page_size"], max_ctx_len=max_ctx_len, scale=inp["scale"],
-                          o_dtype=o_dtype, out=out, lse=lse)
+                          o_dtype=o_dtype, out=out, lse=lse, debug_flags=debug_flags)
     torch.cuda.synchronize()
     return O, L
 
 
-def oracle_attn(inp, rows=None):
+def oracle_attn(inp, rows=None, max_ctx_len=None):
     return oracle.block_attn(inp["Q"], inp["Kc"], inp["Vc"], inp["page_table"], inp["ctx_len"], inp.get("Kd"),
-                             inp.get("Vd"), page_size=inp["page_size"], scale=inp["scale"], rows=rows)
+                             inp.get("Vd"), page_size=inp["page_size"], scale=inp["scale"], rows=rows,
+                             max_ctx_len=max_ctx_len)
 
 
 def check_attn(O_gpu, L_gpu, O_ref, L_ref, dtype, what=""):

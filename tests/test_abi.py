@@ -19,7 +19,7 @@ FAKE = 0x1000  # never dereferenced: every call below must fail validation first
 
 def test_library_loads_and_reports_version():
     L = _lib.lib()
-    assert L.tt_abi_version() == 2
+    assert L.tt_abi_version() == 3
 
 
 def test_exports_every_header_function():
@@ -78,6 +78,10 @@ def call_attn(p, ws=None, nbytes=0):
     (dict(B=1 << 13, page_size=1024, max_ctx_len=1 << 26, max_pages=1 << 16), 2),  # 2^34 tiles
     (dict(q_stride_b=1 << 31), 4), (dict(o_stride_s=1 << 32), 4),  # strides must fit 31 bits
     (dict(B=1 << 15, max_pages=1 << 15), 4),  # page table past 2^30 entries
+    # offsets inside one sequence are 32-bit byte offsets: (S-1)*stride_s + (H-1)*stride_h + d < 2^30
+    (dict(q_stride_s=1 << 27), 4), (dict(o_stride_s=1 << 27), 4), (dict(den_stride_s=1 << 27), 4),
+    (dict(q_stride_h=1 << 26), 4),
+    (dict(q_stride_s=1 << 25, o_stride_s=1 << 25, den_stride_s=1 << 25), 5),  # within the bound: valid
 ])
 def test_attn_validation(kw, code):
     rc = call_attn(attn_ok(**kw))
@@ -233,10 +237,105 @@ def test_unmask_sampling_workspace_holds_the_draws():
 
 def test_unmask_sampling_vocabulary_bound():
     """With uniforms a vocabulary split may hold at most 2^21 logits. 4096 rows use one split, so
-    V = 2^21 + 512 is refused with TT_ERR_SHAPE, before any launch (the pointers here are fake)."""
+    V = 2^21 + 512 is refused with TT_ERR_SHAPE by the host-side validation. The logits and
+    workspace pointers are NULL: were the bound ever to pass, the call would stop at TT_ERR_NULL
+    and still launch nothing."""
     L = _lib.lib()
     big = (1 << 21) + 512
-    p = unmask_ok(B=256, S=16, V=big, logits_stride_row=big, uniforms=FAKE)
-    nb = L.tt_conf_unmask_workspace_bytes(ctypes.byref(p))
-    assert nb > 0
-    assert L.tt_conf_unmask(ctypes.byref(p), FAKE, nb, None) == 2
+    p = unmask_ok(B=256, S=16, V=big, logits_stride_row=big, uniforms=FAKE, logits=None)
+    assert L.tt_conf_unmask_workspace_bytes(ctypes.byref(p)) == 0
+    assert L.tt_conf_unmask(ctypes.byref(p), None, 0, None) == 2
+    # the same vocabulary without uniforms, or a vocabulary within the bound, is not refused for its size
+    assert L.tt_conf_unmask(ctypes.byref(unmask_ok(B=256, S=16, V=big, logits_stride_row=big, logits=None)),
+                            None, 0, None) == 1
+    ok = (1 << 21)
+    assert L.tt_conf_unmask(ctypes.byref(unmask_ok(B=256, S=16, V=ok, logits_stride_row=ok, uniforms=FAKE,
+                                                   logits=None)), None, 0, None) == 1
+
+
+# --------------------------------------------------------------------------- the Python binding
+
+def _cpu_attn_tensors(B=2, S=16, Hq=32, Hkv=2, D=128, P=16, pages=8, max_pages=4):
+    import torch
+    bf = torch.bfloat16
+    return dict(Q=torch.zeros(B, S, Hq, D, dtype=bf), Kc=torch.zeros(pages, Hkv, P, D, dtype=bf),
+                Vc=torch.zeros(pages, Hkv, P, D, dtype=bf),
+                page_table=torch.zeros(B, max_pages, dtype=torch.int32),
+                ctx_len=torch.zeros(B, dtype=torch.int32), Kd=torch.zeros(B, S, Hkv, D, dtype=bf),
+                Vd=torch.zeros(B, S, Hkv, D, dtype=bf))
+
+
+@pytest.mark.parametrize("change", [
+    "Kc_head_dim", "Vc_shape", "Kd_shape", "Vd_shape", "ctx_len_shape", "table_rows", "Kd_without_Vd",
+    "cache_dtype", "out_shape", "lse_shape", "lse_dtype", "debug_dtype",
+])
+def test_attn_params_rejects_mismatched_tensors(change):
+    """attn_params checks shapes and dtypes before anything reaches the library (CPU tensors: the
+    checks come before any pointer is used)."""
+    import torch
+    from attention_eq_block_amd import api
+    t = _cpu_attn_tensors()
+    kw = {}
+    if change == "Kc_head_dim":
+        t["Kc"] = torch.zeros(8, 2, 16, 64, dtype=torch.bfloat16)
+        t["Vc"] = t["Kc"].clone()
+    elif change == "Vc_shape":
+        t["Vc"] = torch.zeros(7, 2, 16, 128, dtype=torch.bfloat16)
+    elif change == "Kd_shape":
+        t["Kd"] = torch.zeros(2, 15, 2, 128, dtype=torch.bfloat16)
+    elif change == "Vd_shape":
+        t["Vd"] = torch.zeros(2, 16, 1, 128, dtype=torch.bfloat16)
+    elif change == "ctx_len_shape":
+        t["ctx_len"] = torch.zeros(3, dtype=torch.int32)
+    elif change == "table_rows":
+        t["page_table"] = torch.zeros(1, 4, dtype=torch.int32)
+    elif change == "Kd_without_Vd":
+        t["Vd"] = None
+    elif change == "cache_dtype":
+        t["Kc"] = t["Kc"].float()
+        t["Vc"] = t["Vc"].float()
+    elif change == "out_shape":
+        kw["out"] = torch.zeros(2, 16, 32, 64, dtype=torch.bfloat16)
+    elif change == "lse_shape":
+        kw["lse"] = torch.zeros(2, 16, 32)
+    elif change == "lse_dtype":
+        kw["lse"] = torch.zeros(2, 32, 16, dtype=torch.float64)
+    elif change == "debug_dtype":
+        kw["debug_flags"] = torch.zeros(1, dtype=torch.int64)
+    with pytest.raises((ValueError, TypeError)):
+        api.attn_params(t["Q"], t["Kc"], t["Vc"], t["page_table"], t["ctx_len"], t["Kd"], t["Vd"], page_size=16,
+                        max_ctx_len=64, **kw)
+
+
+def test_attn_params_accepts_matching_tensors():
+    from attention_eq_block_amd import api
+    t = _cpu_attn_tensors()
+    p = api.attn_params(t["Q"], t["Kc"], t["Vc"], t["page_table"], t["ctx_len"], t["Kd"], t["Vd"], page_size=16,
+                        max_ctx_len=64)
+    assert p.B == 2 and p.Hkv == 2 and p.debug_flags is None
+
+
+@pytest.mark.parametrize("change", ["conf_dtype", "conf_shape", "num_masked_dtype", "num_masked_shape",
+                                    "mask_out_dtype", "mask_out_shape"])
+def test_unmask_params_rejects_mismatched_tensors(change):
+    import torch
+    from attention_eq_block_amd import api
+    B, S, V = 2, 16, 1000
+    x = torch.zeros(B, S, V, dtype=torch.bfloat16)
+    mask = torch.ones(B, S, dtype=torch.uint8)
+    tokens = torch.zeros(B, S, dtype=torch.int32)
+    kw = {}
+    if change == "conf_dtype":
+        kw["conf"] = torch.zeros(B, S, dtype=torch.float64)
+    elif change == "conf_shape":
+        kw["conf"] = torch.zeros(B, S + 1)
+    elif change == "num_masked_dtype":
+        kw["num_masked"] = torch.zeros(B, dtype=torch.int64)
+    elif change == "num_masked_shape":
+        kw["num_masked"] = torch.zeros(B, S, dtype=torch.int32)
+    elif change == "mask_out_dtype":
+        kw["mask_out"] = torch.zeros(B, S, dtype=torch.int32)
+    elif change == "mask_out_shape":
+        kw["mask_out"] = torch.zeros(B, S - 1, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        api.unmask_params(x, mask, tokens, gamma=0.8, temperature=0.1, steps_left=16, **kw)

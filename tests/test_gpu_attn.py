@@ -1,8 +1,9 @@
 """tt_block_attn and tt_lse_merge on the GPU against the float64 oracle.
 
-Eq. (1) of Nemotron-TwoTower (arXiv 2606.26493, section 2.1). Small shapes are
-compared element by element; full-size workloads (in the launch configuration the
-benchmark times) on sampled rows. Tolerances are stated in parity.py.
+Eq. (1) of Nemotron-TwoTower (arXiv 2606.26493, section 2.1). Every shape, the
+full-size workloads included (in the launch configuration the benchmark times), is
+compared element by element over all of O and LSE, rel-L2 over the whole tensor.
+Tolerances are stated in parity.py.
 """
 import math
 
@@ -13,7 +14,7 @@ import torch
 import oracle
 from attention_eq_block_amd import api, synth
 
-from parity import check_attn, check_attn_rows, gpu_attn, oracle_attn, sample_rows, to_dev
+from parity import check_attn, gpu_attn, oracle_attn, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -42,13 +43,13 @@ def test_single_bf16(variant):
     print(run_full(synth.attn_case("single", variant)))
 
 
-def test_ragged_bf16_full_size_sampled():
-    """B=64, prefix 16*U{32..512}, shuffled 16-token pages; sampled rows at full size."""
+def test_ragged_bf16_full_size():
+    """B=64, prefix 16*U{32..512}, shuffled 16-token pages: every row at full size."""
     c = synth.attn_case("ragged")
     inp = synth.make_attn_inputs(c, seed=0)
     O, L = gpu_attn(inp, max_ctx_len=c.max_ctx_len)
-    rows = sample_rows(c.B, c.Hq, c.S, 1500, seed=1)
-    print(check_attn_rows(O, L, inp, rows, c.dtype, "ragged"))
+    Or, Lr = oracle_attn(inp)
+    print(check_attn(O, L, Or, Lr, c.dtype, "ragged"))
 
 
 def test_ragged_unscaled_small_full_compare():
@@ -56,22 +57,49 @@ def test_ragged_unscaled_small_full_compare():
     print(run_full(c))
 
 
-def test_long_bf16_full_size_sampled():
-    """B=4, prefix 131072, S=32 (two row blocks per kv head); sampled rows."""
+def test_long_bf16_full_size():
+    """B=4, prefix 131072, S=32 (two row blocks per kv head): every row."""
     c = synth.attn_case("long")
     inp = synth.make_attn_inputs(c, seed=0)
     O, L = gpu_attn(inp, max_ctx_len=131072)
-    rows = sample_rows(c.B, c.Hq, c.S, 160, seed=2)
-    print(check_attn_rows(O, L, inp, rows, c.dtype, "long"))
+    Or, Lr = oracle_attn(inp)
+    print(check_attn(O, L, Or, Lr, c.dtype, "long"))
 
 
-def test_loop_layer_full_size_sampled():
-    """B=32, prefix 8192, S=16: one of the six layer caches of the denoise loop."""
+def test_loop_layer_full_size():
+    """B=32, prefix 8192, S=16: one of the six layer caches of the denoise loop, every row."""
     c = synth.attn_case("loop")
     inp = synth.make_attn_inputs(c, seed=0, layer=3)
     O, L = gpu_attn(inp, max_ctx_len=8192)
-    rows = sample_rows(c.B, c.Hq, c.S, 600, seed=3)
-    print(check_attn_rows(O, L, inp, rows, c.dtype, "loop"))
+    Or, Lr = oracle_attn(inp)
+    print(check_attn(O, L, Or, Lr, c.dtype, "loop"))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_out_of_range_lengths_and_page_ids(dtype):
+    """ctx_len below 0 and above max_ctx_len, and page ids below 0 and past the pool, read as their
+    clamp into range (the library's stated behaviour, which the oracle implements); debug mode
+    reports both kinds in the flags word, and a clean call leaves it 0."""
+    c = case(5, 16, 32, 2, 128, [300, 64, 500, 129, 200], dtype=dtype, shuffle_pages=True, spare_pages=2)
+    inp = synth.make_attn_inputs(c, seed=11)
+    max_ctx = 400
+    num_pages = inp["Kc"].shape[0]
+    flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+    O, L = gpu_attn(inp, max_ctx_len=max_ctx, debug_flags=flags)
+    assert int(flags.item()) == 0, "clean data raised debug flags"
+    cl = torch.tensor([-7, 64, 500, 129, 1 << 30], dtype=torch.int32)
+    pt = inp["page_table"].clone()
+    pt[1, 0] = -5                   # a page sequence 1 reads
+    pt[3, 8] = num_pages + 3        # the page of sequence 3's last key (128)
+    bad = dict(inp, ctx_len=cl, page_table=pt)
+    flags.zero_()
+    O, L = gpu_attn(bad, max_ctx_len=max_ctx, debug_flags=flags)
+    assert int(flags.item()) == 3, f"debug flags {int(flags.item())}, want TT_DEBUG_CTX_LEN | TT_DEBUG_PAGE_ID"
+    Or, Lr = oracle_attn(bad, max_ctx_len=max_ctx)
+    print(check_attn(O, L, Or, Lr, dtype, "clamped data"))
+    # without debug mode the outputs are the same and nothing is reported
+    O2, L2 = gpu_attn(bad, max_ctx_len=max_ctx)
+    assert torch.equal(O2, O) and torch.equal(L2, L)
 
 
 # --------------------------------------------------------------------------- edge cases
