@@ -17,8 +17,16 @@ temperature 0.1. The JSON line reports noisy-block tokens per second per
 attention layer (B*S*layers*steps / time), the attention call's roofline, and
 the CPU oracle on a bounded sample as a baseline.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload loop|single|ragged|long]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload loop|tiny|single|ragged|long|...]
     python bench.py --copy-calibration   # a plain device copy of known size, for counter scaling
+
+The default run (loop workload) also times the other four workloads and reports them in
+"per_config", one entry per workload: the tiny fp32 call and its unmask step (us), the
+single-layer call cold (a 512 MB buffer rewritten before each call) and warm, the ragged
+batch and its 64 x 16 x 131072 unmask step, and the long-prefix call against the bf16 MFMA
+roof; every entry has the median, p10 and p90 of at least 20 calls timed one by one and the
+oracle on a bounded sample at one thread and at every host thread. The loop itself also runs
+at gamma 0.5 and 0.95 (blocks/s and steps per block).
 
 roofline.traffic is the HBM traffic of one attention call measured with
 rocprofv3 FETCH_SIZE / WRITE_SIZE counters, scaled by the ratio the same
@@ -75,10 +83,54 @@ def measured_traffic():
     except (KeyError, ValueError):
         return None
 METRIC = "noisy-block tokens/s per attn layer (S=16); achieved HBM TB/s vs peak"
+MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+SCRUB_BYTES = 512 << 20    # written between timed calls so that the next one reads HBM, not the 256 MB MALL
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def pct(xs, q):
+    """q-th percentile (0..100) of a list, linear interpolation."""
+    ys = sorted(xs)
+    if not ys:
+        return float("nan")
+    k = (len(ys) - 1) * q / 100.0
+    lo, hi = int(math.floor(k)), int(math.ceil(k))
+    return ys[lo] + (ys[hi] - ys[lo]) * (k - lo)
+
+
+def spread_us(ms):
+    """median, p10 and p90 of per-call times (ms) in microseconds."""
+    return {"median": pct(ms, 50) * 1e3, "p10": pct(ms, 10) * 1e3, "p90": pct(ms, 90) * 1e3, "n": len(ms)}
+
+
+class Scrub:
+    """A 512 MB buffer rewritten between timed calls (outside their events)."""
+
+    def __init__(self):
+        self.buf = torch.empty(SCRUB_BYTES // 4, dtype=torch.float32, device="cuda")
+        self.k = 0
+
+    def __call__(self):
+        self.k += 1
+        self.buf.fill_(float(self.k))
+
+
+def time_each(call, stream, reps, warmup, scrub=None):
+    """Per-call times (ms): HIP events on the stream the kernels run on, around each call only."""
+    for _ in range(warmup):
+        call()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        if scrub is not None:
+            scrub()
+        e0.record(stream)
+        call()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in ev]
 
 
 class Layer:
@@ -93,7 +145,8 @@ class Layer:
                                  scale=inp["scale"])
         self.out, self.lse = self.p._keep
         nb = api.block_attn_workspace_bytes(self.p)
-        self.ws = workspace if workspace is not None else torch.empty(nb, dtype=torch.uint8, device="cuda")
+        self.ws = workspace if workspace is not None else torch.empty(max(nb, 16), dtype=torch.uint8,
+                                                                      device="cuda")
         self.nb = nb
 
     def __call__(self, stream):
@@ -101,51 +154,228 @@ class Layer:
         if rc:
             raise RuntimeError(f"tt_block_attn failed: {api.status_string(rc)}")
 
+    def cpu_sub(self, b0, b1):
+        """The inputs of sequences b0..b1-1 on the CPU (their pages only)."""
+        inp = self.inp
+        pages = inp["page_table"][b0:b1].cpu()
+        used = pages[pages >= 0]
+        lo, hi = int(used.min()), int(used.max()) + 1
+        return dict(Q=inp["Q"][b0:b1].cpu(), Kc=inp["Kc"][lo:hi].cpu(), Vc=inp["Vc"][lo:hi].cpu(),
+                    page_table=torch.where(pages >= 0, pages - lo, pages).to(torch.int32),
+                    ctx_len=inp["ctx_len"][b0:b1].cpu(),
+                    Kd=None if inp["Kd"] is None else inp["Kd"][b0:b1].cpu(),
+                    Vd=None if inp["Vd"] is None else inp["Vd"][b0:b1].cpu(), page_size=inp["page_size"],
+                    scale=inp["scale"])
 
-def cpu_baseline_loop(layers, logits, case, ucase, budget_s=12.0, uniforms=None):
-    """The float64 oracle on whole sequences of the same workload (one layer's attention
-    per sequence plus one unmask step), scaled to tokens/s per attention layer."""
+
+def oracle_attn_time(d, rows=None, threads=None):
+    """Seconds the float64 oracle takes for Eq. (1) over the given inputs (all rows or a sample)."""
     import oracle
-
-    S = case.S
-    L0 = layers[0].inp
-    per = case.pages_of(case.ctx_lens[0])
-
-    def sub(b0, b1):
-        pages = L0["page_table"][b0:b1].cpu()
-        lo = int(pages.min())
-        hi = int(pages.max()) + 1
-        return dict(Q=L0["Q"][b0:b1].cpu(), Kc=L0["Kc"][lo:hi].cpu(), Vc=L0["Vc"][lo:hi].cpu(),
-                    page_table=(pages - lo).to(torch.int32), ctx_len=L0["ctx_len"][b0:b1].cpu(),
-                    Kd=L0["Kd"][b0:b1].cpu(), Vd=L0["Vd"][b0:b1].cpu())
-
-    def run(n):
-        d = sub(0, n)
-        t0 = time.perf_counter()
-        oracle.block_attn(d["Q"], d["Kc"], d["Vc"], d["page_table"], d["ctx_len"], d["Kd"], d["Vd"],
-                          page_size=case.page_size, scale=1.0 / math.sqrt(case.D))
-        t1 = time.perf_counter()
-        x = logits[0][:n].cpu()
-        tok, mk = synth.make_mask_state(n, S)
-        oracle.conf_unmask(x, mk, tok, gamma=oracle.f32(ucase.gamma), temperature=oracle.f32(ucase.temperature),
-                           steps_left=synth.LOOP_STEPS, uniforms=None if uniforms is None else uniforms[:n].cpu())
-        t2 = time.perf_counter()
-        return t1 - t0, t2 - t1
-
-    ta, tu = run(1)
-    n = max(1, min(case.B, int(budget_s / max(1e-3, synth.LOOP_LAYERS * ta + tu))))
-    if n > 1:
-        ta, tu = run(n)
-    per_seq_step = synth.LOOP_LAYERS * ta + tu  # one denoising step of n sequences (6 layers + unmask)
-    value = n * S * synth.LOOP_LAYERS / per_seq_step
-    del per
-    return dict(value=value, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
-                sample=f"{n} of {case.B} sequences: one layer's Eq. (1) attention (prefix {case.ctx_lens[0]}, "
-                       f"S={S}, 32/2 heads, d={case.D}) timed {ta:.2f} s and one unmask step timed {tu:.2f} s; "
-                       f"a denoising step counted as 6 attention layers plus one unmask")
+    if threads is not None:
+        oracle.set_num_threads(threads)
+    t0 = time.perf_counter()
+    oracle.block_attn(d["Q"], d["Kc"], d["Vc"], d["page_table"], d["ctx_len"], d["Kd"], d["Vd"],
+                      page_size=d["page_size"], scale=d["scale"], rows=rows)
+    return time.perf_counter() - t0
 
 
-def run_loop(args):
+def host_threads():
+    import oracle
+    oracle.set_num_threads(max(1, len(os.sched_getaffinity(0))))
+    return oracle.num_threads()
+
+
+def attn_roofline(case, call_ms, bound):
+    """Roofline of one attention call: algorithmic bytes against HBM, or flops against bf16 MFMA."""
+    if bound == "mfma":
+        ach = case.flops() / (call_ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": ach, "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / MFMA_PEAK_TFLOPS, "traffic": None, "flops": case.flops(),
+                "hbm_frac": case.algorithmic_bytes() / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    ach = case.algorithmic_bytes() / (call_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+            "traffic": None, "algorithmic_bytes": case.algorithmic_bytes()}
+
+
+def unmask_timing(ucase, stream, args, scrub, logits=None):
+    """One ConfidenceSample step over all-masked rows (mask_out separate, so every call sees the same
+    state), timed per call; bytes are the masked logit rows read once."""
+    B, S = ucase.B, ucase.S
+    x = logits if logits is not None else synth.make_logits(ucase, seed=0, device="cuda")
+    mask = torch.ones(B, S, dtype=torch.uint8, device="cuda")
+    mask_out = torch.empty_like(mask)
+    tokens = torch.full((B, S), synth.MASK_TOKEN_ID, dtype=torch.int32, device="cuda")
+    p = api.unmask_params(x, mask, tokens, gamma=ucase.gamma, temperature=ucase.temperature, steps_left=16,
+                          mask_out=mask_out)
+    ws = torch.empty(max(16, api.conf_unmask_workspace_bytes(p)), dtype=torch.uint8, device="cuda")
+    lib = api.lib()
+    sh = stream.cuda_stream
+
+    def call():
+        rc = lib.tt_conf_unmask(p, ws.data_ptr(), ws.numel(), sh)
+        if rc:
+            raise RuntimeError(f"tt_conf_unmask failed: {api.status_string(rc)}")
+
+    ms = time_each(call, stream, max(20, args.reps), 5, scrub)
+    med = pct(ms, 50)
+    algo = ucase.algorithmic_bytes(B * S)
+    ach = algo / (med * 1e-3) / 1e9
+    return x, {"rows": B * S, "V": ucase.V, "call_us": spread_us(ms), "masked_rows_per_s": B * S / (med * 1e-3),
+               "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": ach / HBM_PEAK_GBS, "algorithmic_bytes": algo}}
+
+
+def oracle_unmask_time(x, ucase, threads=None):
+    import oracle
+    if threads is not None:
+        oracle.set_num_threads(threads)
+    tok, mk = synth.make_mask_state(x.shape[0], x.shape[1])
+    t0 = time.perf_counter()
+    oracle.conf_unmask(x, mk, tok, gamma=oracle.f32(ucase.gamma), temperature=oracle.f32(ucase.temperature),
+                       steps_left=16)
+    return time.perf_counter() - t0
+
+
+# --------------------------------------------------------------------------- single-call workloads
+
+CONFIG_OF = {"tiny": "C1", "single": "C2", "ragged": "C3", "long": "C4", "loop": "C5"}
+
+
+def run_single(args, name, stream):
+    """One attention layer of a workload, timed call by call (median, p10, p90). 'single' is also
+    timed warm (no scrub: its 4.5 MB stay in the MALL); 'ragged' and 'tiny' add their unmask step;
+    'long' is reported against the bf16 MFMA roof, the others against HBM."""
+    case = synth.attn_case(name)
+    L = Layer(case, 0)
+    scrub = Scrub()
+    sh = stream.cuda_stream
+    reps = max(20, args.reps)
+    ms = time_each(lambda: L(sh), stream, reps, 5, None if name == "tiny" else scrub)
+    med = pct(ms, 50)
+    bound = "mfma" if name == "long" else "hbm"
+    res = {"config": CONFIG_OF[name], "metric": METRIC, "value": case.B * case.S / (med * 1e-3),
+           "unit": "tokens/s", "dtype": "f32" if case.dtype == torch.float32 else "bf16",
+           "workload": f"single attention layer, {name}: B={case.B}, S={case.S}, {case.Hq}/{case.Hkv} heads, "
+                       f"d={case.D}, prefix {case.max_ctx_len}" + (" (ragged, shuffled pages)" if name == "ragged"
+                                                                   else ""),
+           "call_us": spread_us(ms), "tflops": case.flops() / (med * 1e-3) / 1e12,
+           "roofline": attn_roofline(case, med, bound),
+           "timing": "per call between HIP events; a 512 MB buffer rewritten before each call"
+           if name != "tiny" else "per call between HIP events"}
+    if name == "tiny":
+        res["roofline"] = {"bound": "latency", "note": "66 KB per call: launch latency, reported in us"}
+    if name == "single":
+        wm = time_each(lambda: L(sh), stream, reps, 5, None)
+        res["warm_call_us"] = spread_us(wm)
+        res["warm_value"] = case.B * case.S / (pct(wm, 50) * 1e-3)
+        res["warm_roofline"] = attn_roofline(case, pct(wm, 50), "hbm")
+        res["warm_note"] = "back to back: the 4.5 MB working set stays in the 256 MB MALL"
+    ucase = None
+    if name in ("tiny", "ragged"):
+        ucase = synth.unmask_case(name, temperature=args.temperature, gamma=args.gamma)
+        x, res["unmask"] = unmask_timing(ucase, stream, args, None if name == "tiny" else scrub)
+    del scrub
+    if not args.no_cpu:
+        res["cpu_baseline"] = single_cpu_baseline(name, case, L, med, x if ucase is not None else None, ucase)
+    return res
+
+
+def single_cpu_baseline(name, case, L, gpu_ms, logits, ucase):
+    """The float64 oracle on a bounded sample of the same call, at one thread and at every host
+    thread, scaled to the same unit (tokens/s per attention layer)."""
+    import oracle
+    B, S, Hq = case.B, case.S, case.Hq
+    nth = host_threads()
+    out = {"kind": "oracle", "unit": "tokens/s"}
+    if name in ("tiny", "single"):
+        d = L.cpu_sub(0, B)
+        t1 = oracle_attn_time(d, threads=1)
+        tn = oracle_attn_time(d, threads=nth)
+        out.update(value=B * S / tn, cores=nth, one_thread=B * S / t1, sample="the whole call")
+        if logits is not None:
+            out["unmask_s"] = {"1": oracle_unmask_time(logits.cpu(), ucase, 1),
+                               str(nth): oracle_unmask_time(logits.cpu(), ucase, nth)}
+    elif name == "ragged":
+        n = 4
+        d = L.cpu_sub(0, n)
+        keys = int(d["ctx_len"].sum()) + n * S
+        frac = keys / (sum(case.ctx_lens) + B * S)  # share of the call's work
+        tn = oracle_attn_time(d, threads=nth)
+        rows1 = oracle.all_rows(1, Hq, S)
+        t1 = oracle_attn_time(L.cpu_sub(0, 1), rows=rows1, threads=1)
+        frac1 = (int(case.ctx_lens[0]) + S) / (sum(case.ctx_lens) + B * S)
+        out.update(value=B * S / (tn / frac), cores=nth, one_thread=B * S / (t1 / frac1),
+                   sample=f"{n} of {B} sequences at {nth} threads, 1 sequence at 1 thread, scaled by their share "
+                          f"of the call's keys")
+        xs = logits[:n].cpu()
+        tu = oracle_unmask_time(xs, ucase, nth)
+        out["unmask"] = {"masked_rows_per_s": n * S / tu, "cores": nth,
+                         "sample": f"{n} of {B} sequences (all {n * S} rows masked)"}
+    else:  # long: a sample of rows of sequence 0
+        d = L.cpu_sub(0, 1)
+        rows_n = oracle.all_rows(1, Hq, S)
+        tn = oracle_attn_time(d, rows=rows_n, threads=nth)
+        rows_1 = rows_n[:: 16]
+        t1 = oracle_attn_time(d, rows=rows_1, threads=1)
+        total = B * Hq * S
+        out.update(value=B * S / (tn * total / len(rows_n)), cores=nth,
+                   one_thread=B * S / (t1 * total / len(rows_1)),
+                   sample=f"{len(rows_n)} of {total} query rows at {nth} threads, {len(rows_1)} at 1 thread, "
+                          f"scaled to the whole call")
+    oracle.set_num_threads(nth)
+    out["vs_gpu"] = "gpu/oracle = %.0fx" % ((B * S / (gpu_ms * 1e-3)) / out["value"])
+    return out
+
+
+# --------------------------------------------------------------------------- the denoise loop
+
+
+def cpu_baseline_loop(layers, logits, case, ucase, steps_gpu, budget_s=12.0, uniforms=None):
+    """The float64 oracle running one whole block of Algorithm 2 (gamma and temperature of the run)
+    on n of the B sequences at every host thread: T steps of six Eq. (1) layers plus one
+    ConfidenceSample, stopping when the block is clean. Also one step of one sequence at one thread.
+    Reported in the same unit: noisy tokens per second per attention layer."""
+    import oracle
+    S, T, NL = case.S, synth.LOOP_STEPS, synth.LOOP_LAYERS
+    nth = host_threads()
+    one = [L.cpu_sub(0, 1) for L in layers]
+    t1 = oracle_attn_time(one[0], threads=1)
+    tu1 = oracle_unmask_time(logits[0][:1].cpu(), ucase, 1)
+    step1 = NL * t1 + tu1
+    oracle.set_num_threads(nth)
+    tn = oracle_attn_time(one[0], threads=nth)
+    n = max(1, min(case.B, int(budget_s / max(1e-3, steps_gpu * NL * tn))))
+    subs = [L.cpu_sub(0, n) for L in layers]
+    xs = [lg[:n].cpu() for lg in logits]
+    us = None if uniforms is None else [u[:n].cpu() for u in uniforms]
+    tok, mk = synth.make_mask_state(n, S)
+    tok, mk = tok.numpy(), mk.numpy()
+    t0 = time.perf_counter()
+    steps = 0
+    for r in range(1, T + 1):
+        for d in subs:
+            oracle.block_attn(d["Q"], d["Kc"], d["Vc"], d["page_table"], d["ctx_len"], d["Kd"], d["Vd"],
+                              page_size=d["page_size"], scale=d["scale"])
+        res = oracle.conf_unmask(xs[r - 1], mk, tok, gamma=oracle.f32(ucase.gamma),
+                                 temperature=oracle.f32(ucase.temperature), steps_left=T - r + 1,
+                                 uniforms=None if us is None else us[r - 1])
+        tok, mk = res["tokens"], res["mask"]
+        steps = r
+        if int(mk.sum()) == 0:
+            break
+    wall = time.perf_counter() - t0
+    return dict(value=n * S * NL * steps / wall, unit="tokens/s", cores=nth, kind="oracle",
+                sample=f"one whole block of Algorithm 2 on {n} of {case.B} sequences ({steps} steps of 6 Eq. (1) "
+                       f"layers plus one ConfidenceSample, prefix {case.ctx_lens[0]}, S={S}, 32/2 heads, d={case.D}) "
+                       f"in {wall:.1f} s at {nth} threads",
+                blocks_per_s=n / wall, steps_per_block=steps,
+                one_thread={"value": S * NL / step1, "unit": "tokens/s", "cores": 1,
+                            "sample": f"one denoising step of 1 sequence (6 layers at {t1:.2f} s each, unmask "
+                                      f"{tu1:.3f} s); extrapolated to a block by its step count"},
+                per_step_s_all_threads=wall / steps)
+
+
+def run_loop(args, stream):
     case = synth.attn_case("loop")
     ucase = synth.unmask_case("loop", temperature=args.temperature, gamma=args.gamma)
     B, S, T, NL = case.B, case.S, synth.LOOP_STEPS, synth.LOOP_LAYERS
@@ -166,13 +396,13 @@ def run_loop(args):
                            steps_left=T, num_masked=nmask, uniforms=unis[0] if unis else None)
     uws = torch.empty(max(16, api.conf_unmask_workspace_bytes(up)), dtype=torch.uint8, device="cuda")
     lib = api.lib()
-    stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(T)]
 
-    def block(timing=False):
+    def block(gamma, timing=False):
         tokens.fill_(synth.MASK_TOKEN_ID)
         mask.fill_(1)
+        up.gamma = gamma
         steps = 0
         for r in range(1, T + 1):
             if timing:
@@ -195,81 +425,71 @@ def run_loop(args):
                 break
         return steps
 
-    log("[bench] warmup")
-    for _ in range(args.warmup):
-        block()
-    torch.cuda.synchronize()
-    log("[bench] timed")
-    attn_ms, n_attn_steps, total_steps = 0.0, 0, 0
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        n = block(timing=True)
-        total_steps += n
+    def timed_blocks(gamma, k, warmup):
+        for _ in range(warmup):
+            block(gamma)
         torch.cuda.synchronize()
-        for r in range(n):
-            attn_ms += ev[r][0].elapsed_time(ev[r][1])
-        n_attn_steps += n
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+        per_call, total_steps = [], 0
+        t0 = time.perf_counter()
+        for _ in range(k):
+            n = block(gamma, timing=True)
+            total_steps += n
+            torch.cuda.synchronize()
+            per_call += [ev[r][0].elapsed_time(ev[r][1]) / NL for r in range(n)]
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, total_steps, per_call
+
+    log("[bench] warmup and timed blocks")
+    wall, total_steps, per_call = timed_blocks(args.gamma, args.steps, args.warmup)
     ms_per_block = wall * 1e3 / args.steps
     steps_per_block = total_steps / args.steps
     value = B * S * NL * total_steps / wall
-    call_ms = attn_ms / (n_attn_steps * NL)
+    call_ms = sum(per_call) / len(per_call)
     algo = case.algorithmic_bytes()
     achieved = algo / (call_ms * 1e-3) / 1e9
     assert torch.isfinite(layers[0].out.float()).all()
     log(f"[bench] {steps_per_block:.2f} steps/block, {ms_per_block:.3f} ms/block, attention call {call_ms * 1e3:.1f} us")
+    sweep = {}
+    if not args.sample and math.isfinite(args.gamma):
+        for g in (0.5, 0.8, 0.95):
+            if g == args.gamma:
+                sweep[str(g)] = {"blocks_per_s": B * args.steps / wall, "steps_per_block": steps_per_block,
+                                 "tokens_per_s": value}
+                continue
+            k = max(3, args.steps // 2)
+            w, ts, _ = timed_blocks(g, k, 1)
+            sweep[str(g)] = {"blocks_per_s": B * k / w, "steps_per_block": ts / k,
+                             "tokens_per_s": B * S * NL * ts / w}
+    wl = ("full-block denoise loop (Algorithm 2): batch 32, S=16, T=16, 6 attention layers, prefix 8192, "
+          f"32 q / 2 kv heads, head_dim 128, V=131072, gamma {args.gamma:g}, temperature {args.temperature:g}"
+          + (", stochastic draws" if args.sample else ""))
     res = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_block, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "full-block denoise loop (Algorithm 2): batch 32, S=16, T=16, 6 attention layers, "
-                               "prefix 8192, 32 q / 2 kv heads, head_dim 128, V=131072, "
-                               f"gamma {args.gamma:g}, temperature {args.temperature:g}"
-                               + (", stochastic draws" if args.sample else ""),
-                   "global_batch": B, "seq_len": case.ctx_lens[0] + S, "parallelism": "none",
+        "config": {"workload": wl, "global_batch": B, "seq_len": case.ctx_lens[0] + S, "parallelism": "none",
                    "denoise_steps_per_block": steps_per_block, "blocks_per_s": B * args.steps / wall,
-                   "attn_call_us": call_ms * 1e3, "attn_call_tokens_per_s": B * S / (call_ms * 1e-3)},
+                   "attn_call_us": call_ms * 1e3, "attn_call_tokens_per_s": B * S / (call_ms * 1e-3),
+                   "attn_call_us_spread": spread_us(per_call)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": "tt_block_attn (attn_bf16_kernel + attn_bf16_finalize), one layer",
                      "algorithmic_bytes": algo},
     }
+    if sweep:
+        res["config"]["gamma_sweep"] = sweep
     if not args.no_cpu:
-        log("[bench] cpu baseline (oracle)")
-        res["cpu_baseline"] = cpu_baseline_loop(layers, logits, case, ucase, uniforms=unis[0] if unis else None)
-    return res
-
-
-def run_single(args, name):
-    """Diagnostic: one attention layer of another workload (plus its unmask for 'ragged')."""
-    case = synth.attn_case(name)
-    L = Layer(case, 0)
-    stream = torch.cuda.current_stream()
-    sh = stream.cuda_stream
-    for _ in range(args.warmup):
-        L(sh)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        L(sh)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    call_ms = e0.elapsed_time(e1) / args.steps
-    algo = case.algorithmic_bytes()
-    achieved = algo / (call_ms * 1e-3) / 1e9
-    flops = case.flops()
-    res = {"metric": METRIC, "value": case.B * case.S / (call_ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": call_ms, "higher_is_better": True,
-           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-           "config": {"workload": f"single attention layer, {name}: B={case.B}, S={case.S}, "
-                                  f"{case.Hq}/{case.Hkv} heads, d={case.D}, max prefix {case.max_ctx_len}",
-                      "global_batch": case.B, "seq_len": case.max_ctx_len + case.S, "parallelism": "none",
-                      "tflops": flops / (call_ms * 1e-3) / 1e12},
-           "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": achieved / HBM_PEAK_GBS, "traffic": None}}
-    return res
+        log("[bench] cpu baseline (oracle): one whole block")
+        cb = cpu_baseline_loop(layers, [lg for lg in logits], case, ucase, steps_per_block, uniforms=unis)
+        if sweep:
+            # n sequences per measured step: blocks/s = n / (steps at this gamma * seconds per step)
+            n_seq = cb["blocks_per_s"] * cb["steps_per_block"] * cb["per_step_s_all_threads"]
+            cb["gamma_sweep_extrapolated"] = {
+                g: {"blocks_per_s": n_seq / (v["steps_per_block"] * cb["per_step_s_all_threads"]),
+                    "note": "the measured gamma 0.8 step time times the GPU run's step count at this gamma"}
+                for g, v in sweep.items()}
+        res["cpu_baseline"] = cb
+    return res, layers
 
 
 APPEND_METRIC = "committed-block KV rows appended per s (one layer); achieved HBM GB/s vs peak"
@@ -462,12 +682,16 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="loop", choices=["loop", "single", "ragged", "long", "append", "nll", "sample"])
+    ap.add_argument("--workload", default="loop",
+                    choices=["loop", "tiny", "single", "ragged", "long", "append", "nll", "sample"])
+    ap.add_argument("--reps", type=int, default=30, help="timed calls per single-call workload (at least 20)")
     ap.add_argument("--gamma", type=float, default=0.8)
     ap.add_argument("--temperature", type=float, default=0.1)
     ap.add_argument("--sample", action="store_true",
                     help="loop workload: draw tokens at the temperature (caller uniforms) instead of the argmax")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baselines")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="loop workload only: skip the per-config lines of the other four workloads")
     ap.add_argument("--copy-calibration", action="store_true", help="run only the counter-reference copy")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -481,8 +705,23 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
+    stream = torch.cuda.current_stream()
     if args.workload == "loop":
-        res = run_loop(args)
+        res, layers = run_loop(args, stream)
+        del layers
+        if not args.no_configs and not args.sample:
+            per = []
+            for name in ("tiny", "single", "ragged", "long"):
+                log(f"[bench] config {CONFIG_OF[name]} ({name})")
+                torch.cuda.empty_cache()
+                per.append(run_single(args, name, stream))
+            c5 = {"config": "C5", "metric": METRIC, "value": res["value"], "unit": "tokens/s", "dtype": "bf16",
+                  "workload": res["config"]["workload"], "call_us": res["config"]["attn_call_us_spread"],
+                  "blocks_per_s": res["config"]["blocks_per_s"], "roofline": res["roofline"]}
+            if "cpu_baseline" in res:
+                c5["cpu_baseline"] = res["cpu_baseline"]
+            per.append(c5)
+            res["per_config"] = per
     elif args.workload == "append":
         res = run_append(args)
     elif args.workload == "sample":
@@ -490,7 +729,15 @@ def main():
     elif args.workload == "nll":
         res = run_nll(args)
     else:
-        res = run_single(args, args.workload)
+        r = run_single(args, args.workload, stream)
+        res = {"metric": METRIC, "value": r["value"], "unit": "tokens/s", "n_gpus": 1, "steps": max(20, args.reps),
+               "warmup": 5, "ms_per_step": r["call_us"]["median"] / 1e3, "higher_is_better": True,
+               "scaling": "weak", "vs_baseline": None, "dtype": r["dtype"], "data": "synthetic",
+               "config": {k: v for k, v in r.items() if k not in ("roofline", "cpu_baseline", "metric", "value",
+                                                                   "unit", "dtype")},
+               "roofline": r["roofline"]}
+        if "cpu_baseline" in r:
+            res["cpu_baseline"] = r["cpu_baseline"]
     print(json.dumps(res))
 
 

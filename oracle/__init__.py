@@ -52,6 +52,8 @@ def _bind(lib):
     lib.oracle_conf_unmask.argtypes = [_I, _I, _I, _I, ctypes.c_longlong, _P, _P, _P, ctypes.c_double,
                                        ctypes.c_double, _I, _P, _P, _P, _P, _P, _P, _P]
     lib.oracle_num_threads.restype = _I
+    lib.oracle_set_num_threads.restype = None
+    lib.oracle_set_num_threads.argtypes = [_I]
     lib.oracle_kv_append.restype = _I
     lib.oracle_kv_append.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P]
     lib.oracle_masked_nll.restype = _I
@@ -80,6 +82,11 @@ class use_library:
 
 def num_threads() -> int:
     return int(load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads the oracle's parallel loops use from now on."""
+    load().oracle_set_num_threads(int(n))
 
 
 def _raw(t: Optional[torch.Tensor]):

@@ -46,6 +46,15 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Threads of the parallel loops from now on (timing at one thread and at all of them). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /*
  * Eq. (1): Attn(Q_b, [K_ctx(<b); K_den(b)], [V_ctx(<b); V_den(b)]).
  *

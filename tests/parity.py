@@ -4,12 +4,12 @@ the same seeded inputs and compare them to the stated bar.
 Tolerances (attention, Nemotron-TwoTower Eq. 1):
   float32 path:  O max-abs <= 1e-5, LSE max-abs <= 1e-5
   bf16 path:     O max-abs <= 2e-2 and rel-L2 ||O - O_ref|| / ||O_ref|| <= 4e-3 over the
-                 tensor; LSE max-abs <= 4e-3. The kernel rounds the softmax weights P
-                 to bf16 before the P.V product and sums them in fp32 before that
-                 rounding, so O carries the bf16 rounding of P (about 2^-9 relative per
-                 weight) and LSE the fp32 summation error of up to a few thousand
-                 weights below 2^8 each (the running max may trail the true max by up
-                 to 2^8); 4e-3 covers both with margin.
+                 tensor; LSE max-abs <= 1e-4. The kernel rounds the softmax weights P
+                 to bf16 before the P.V product, so O carries the bf16 rounding of P
+                 (about 2^-9 relative per weight; measured rel-L2 0.0025-0.0029 on the
+                 five workloads). LSE is built from the fp32 scores and the fp32 sum of
+                 the unrounded weights: its error is fp32 rounding of a value near
+                 ln(keys) (measured at most 1.4e-6 on every workload), well inside 1e-4.
 Confidence unmask (Algorithm 2): tokens, masks and counts bit-exact, except that a
 sequence is excluded when one of its decisions sits within 1e-6 of a threshold in the
 oracle's float64 values (a confidence within 1e-6 of gamma, or, on the fallback path,
@@ -29,7 +29,7 @@ from attention_eq_block_amd import api, synth
 F32_TOL = 1e-5
 BF16_MAXABS = 2e-2
 BF16_RELL2 = 4e-3
-BF16_LSE = 4e-3
+BF16_LSE = 1e-4
 
 
 def to_dev(inp, device="cuda"):

@@ -85,8 +85,11 @@ def test_out_of_range_lengths_and_page_ids(dtype):
     max_ctx = 400
     num_pages = inp["Kc"].shape[0]
     flags = torch.zeros(1, dtype=torch.int32, device="cuda")
-    O, L = gpu_attn(inp, max_ctx_len=max_ctx, debug_flags=flags)
+    O, L = gpu_attn(inp, max_ctx_len=c.max_ctx_len, debug_flags=flags)
     assert int(flags.item()) == 0, "clean data raised debug flags"
+    flags.zero_()
+    gpu_attn(inp, max_ctx_len=max_ctx, debug_flags=flags)  # sequence 2's 500 keys exceed max_ctx_len
+    assert int(flags.item()) == 1, f"debug flags {int(flags.item())}, want TT_DEBUG_CTX_LEN"
     cl = torch.tensor([-7, 64, 500, 129, 1 << 30], dtype=torch.int32)
     pt = inp["page_table"].clone()
     pt[1, 0] = -5                   # a page sequence 1 reads
