@@ -99,6 +99,8 @@ def lib():
         L.tt_block_attn_workspace_bytes.argtypes = [ctypes.POINTER(BlockAttnParams)]
         L.tt_block_attn.restype = ctypes.c_int
         L.tt_block_attn.argtypes = [ctypes.POINTER(BlockAttnParams), c_ptr, c_size, c_ptr]
+        L.tt_block_attn_noalloc.restype = ctypes.c_int
+        L.tt_block_attn_noalloc.argtypes = [ctypes.POINTER(BlockAttnParams), c_ptr]
         L.tt_lse_merge.restype = ctypes.c_int
         L.tt_lse_merge.argtypes = [ctypes.c_int, c_ptr, c_ptr, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_int, c_ptr, ctypes.c_int, c_ptr, c_ptr]

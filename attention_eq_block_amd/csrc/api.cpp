@@ -186,6 +186,30 @@ tt_status tt_block_attn(const tt_block_attn_params* p, void* workspace, size_t w
     }
 }
 
+tt_status tt_block_attn_noalloc(const tt_block_attn_params* p, hipStream_t stream) {
+    const tt_status v = validate_attn(p);
+    if (v != TT_OK || p->B == 0) return v;
+    try {
+        if (p->dtype == TT_F32) return tt::launch_attn_f32(*p, stream);  // needs no scratch
+        const tt::AttnPlan plan = tt::plan_attn_bf16(*p, device_cu_count());
+        if (plan.ws_total > tt::kNoallocScratchBytes) {
+            if (log_enabled())
+                fprintf(stderr, "[tt] block_attn_noalloc: needs %zu bytes of scratch, the library holds %zu\n",
+                        plan.ws_total, tt::kNoallocScratchBytes);
+            return TT_ERR_WORKSPACE;
+        }
+        tt_status st = TT_OK;
+        void* ws = tt::noalloc_scratch(&st);
+        if (!ws) return st;
+        if (log_enabled())
+            fprintf(stderr, "[tt] block_attn_noalloc bf16 B=%d S=%d Hq=%d Hkv=%d d=%d Lmax=%d seg=%d ws=%zu\n", p->B,
+                    p->S, p->Hq, p->Hkv, p->head_dim, p->max_ctx_len, plan.n_seg, plan.ws_total);
+        return tt::launch_attn_bf16(*p, plan, ws, stream);
+    } catch (...) {
+        return TT_ERR_HIP;
+    }
+}
+
 tt_status tt_lse_merge(int P, const float* O_parts, const float* lse_parts, int B, int S, int Hq, int d,
                        void* O_out, tt_dtype o_dtype, float* lse_out, hipStream_t stream) {
     if (P < 1 || B < 0 || S < 1 || Hq < 1 || d < 4 || d % 4 != 0) return TT_ERR_SHAPE;

@@ -39,6 +39,8 @@
 // tile, so it needs one page id per tile. The query rows of the next piece are
 // copied into LDS while the current one is computed, and a finished partial
 // is staged through the same LDS so that its stores write whole rows.
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "tt_internal.h"
@@ -1007,7 +1009,37 @@ __global__ __launch_bounds__(kFinThreads) void attn_bf16_finalize(Args a, const 
         a.LSE[((long long)b * a.Hq + h) * a.S + s] = Wsum > 0.f ? M + __logf(Wsum) : -INFINITY;
 }
 
+// Scratch of the allocation-free entry point: the workspace of tt_block_attn,
+// held by the library. Host code never passes this name to a kernel (on the
+// host it is only a stand-in for the symbol); it uses the device address that
+// noalloc_scratch() looks up once per device.
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
 }  // namespace
+
+void* noalloc_scratch(tt_status* st) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) {
+        *st = TT_ERR_HIP;
+        return nullptr;
+    }
+    void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (ptr) return ptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (ptr) return ptr;
+    // this device's copy of the array, looked up with the device current
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+        *st = TT_ERR_HIP;
+        return nullptr;
+    }
+    g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    return ptr;
+}
 
 AttnPlan plan_attn_bf16(const tt_block_attn_params& p, int n_cu) {
     AttnPlan pl{};
@@ -1023,7 +1055,8 @@ AttnPlan plan_attn_bf16(const tt_block_attn_params& p, int n_cu) {
     if (nseg < 8) nseg = 8;
     pl.n_seg = (int)nseg;
     pl.n_slots = pl.n_seg + pl.n_pairs;
-    pl.ws_part_o = (size_t)pl.n_slots * kRows * p.head_dim * sizeof(float);
+    // partial O is kept in the output's precision
+    pl.ws_part_o = (size_t)pl.n_slots * kRows * p.head_dim * (p.o_dtype == TT_F32 ? 4 : 2);
     pl.ws_part_lse = (size_t)pl.n_slots * kRows * sizeof(float);
     pl.ws_units = ((size_t)(p.B + 1) * sizeof(int) + 255) / 256 * 256;
     pl.ws_total = pl.ws_part_o + pl.ws_part_lse + pl.ws_units + 256;

@@ -37,6 +37,12 @@ struct AttnPlan {
 };
 
 AttnPlan plan_attn_bf16(const tt_block_attn_params& p, int n_cu);
+
+// The allocation-free entry point's scratch: a device array of this many bytes
+// inside the library; noalloc_scratch() returns its address on the current
+// device (looked up on the first call there), or null with *st set.
+constexpr size_t kNoallocScratchBytes = TT_NOALLOC_SCRATCH_BYTES;
+void* noalloc_scratch(tt_status* st);
 tt_status launch_attn_bf16(const tt_block_attn_params& p, const AttnPlan& plan, void* ws,
                            hipStream_t s);
 

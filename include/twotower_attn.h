@@ -168,6 +168,23 @@ size_t tt_block_attn_workspace_bytes(const tt_block_attn_params* p);
 tt_status tt_block_attn(const tt_block_attn_params* p, void* workspace, size_t ws_bytes,
                         hipStream_t stream);
 
+/* Allocation-free variant of tt_block_attn, for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops or harnesses that
+ * forbid allocation). Same parameters, kernels and results as tt_block_attn;
+ * instead of a caller workspace it uses a fixed scratch array of
+ * TT_NOALLOC_SCRATCH_BYTES inside the library, which each GPU the library
+ * runs on holds until the process ends (its address is looked up on the first
+ * call on each device). It calls no allocator. Returns TT_ERR_WORKSPACE,
+ * before launching anything, when tt_block_attn_workspace_bytes(p) exceeds
+ * TT_NOALLOC_SCRATCH_BYTES (at head_dim 128 that allows about 750 (sequence,
+ * kv head, 256-row block) pairs with bf16 output, 250 with float32 output).
+ * Nothing in the array needs clearing between calls. All calls on one GPU
+ * share that GPU's array:
+ * calls that overlap in time on one GPU (different streams, or different
+ * host threads) race and must be ordered by the caller. */
+#define TT_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+tt_status tt_block_attn_noalloc(const tt_block_attn_params* p, hipStream_t stream);
+
 /* ------------------------------------------------------------------------ *
  * Log-sum-exp merge of P partial attentions over disjoint key sets
  * ------------------------------------------------------------------------ *

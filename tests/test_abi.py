@@ -25,6 +25,7 @@ def test_library_loads_and_reports_version():
 def test_exports_every_header_function():
     names = _lib.header_functions()
     assert set(names) == {"tt_abi_version", "tt_status_string", "tt_block_attn", "tt_block_attn_workspace_bytes",
+                          "tt_block_attn_noalloc",
                           "tt_lse_merge", "tt_conf_unmask", "tt_conf_unmask_workspace_bytes", "tt_kv_append",
                           "tt_masked_nll", "tt_masked_nll_workspace_bytes"}
     L = _lib.lib()
@@ -339,3 +340,17 @@ def test_unmask_params_rejects_mismatched_tensors(change):
         kw["mask_out"] = torch.zeros(B, S - 1, dtype=torch.uint8)
     with pytest.raises(ValueError):
         api.unmask_params(x, mask, tokens, gamma=0.8, temperature=0.1, steps_left=16, **kw)
+
+
+def test_noalloc_validates_and_refuses_oversized_calls_before_any_launch():
+    """tt_block_attn_noalloc validates like tt_block_attn, and refuses a call whose workspace would
+    exceed the library's fixed scratch (TT_NOALLOC_SCRATCH_BYTES = 64 MiB) with TT_ERR_WORKSPACE,
+    before touching the device (the pointers here are fake)."""
+    L = _lib.lib()
+    f = L.tt_block_attn_noalloc
+    assert f(None, None) == 1
+    assert f(ctypes.byref(attn_ok(S=0)), None) == 2
+    assert f(ctypes.byref(attn_ok(B=0, Q=None, O=None)), None) == 0
+    big = attn_ok(B=1000, max_pages=1, max_ctx_len=16)
+    assert L.tt_block_attn_workspace_bytes(ctypes.byref(big)) > 64 << 20
+    assert f(ctypes.byref(big), None) == 5
