@@ -27,18 +27,17 @@
 // numbered so that consecutive ones run on the same XCD, which keeps a pair's
 // partials in one L2.
 //
-// Schedule inside a workgroup (ping-pong). Eight waves own 32 query rows each
-// and form two groups of four, so that every SIMD runs one wave of each group.
-// Per tile a wave has a matrix phase (scores of tile i, and the softmax and
-// PV product of tile i-1: MFMAs, LDS reads and the exponentials between them)
-// and a vector phase (mask and row max of tile i, the staging of the next tile
-// into LDS, cursor and address work, the next global loads). Group 1 runs one
-// barrier interval behind group 0, so in every interval one wave on each SIMD
-// issues MFMAs while the other does the vector phase. Group 0 stages the K
-// half of every tile and group 1 the V half; each wave moves 16 keys of a
-// tile, so it needs one page id per tile. The query rows of the next piece are
-// copied into LDS while the current one is computed, and a finished partial
-// is staged through the same LDS so that its stores write whole rows.
+// Schedule inside a workgroup. Eight waves own 32 query rows each; waves
+// 0-3 bring the K half of every tile into LDS and waves 4-7 the V half, each
+// wave 16 keys (one page id) per tile, with direct-to-LDS buffer loads: the
+// data never passes through registers. K and V tiles are double-buffered in
+// LDS: at the start of tile i's phase the K waves request K of tile i+1 and
+// the V waves V of tile i (V is used one tile later), one phase before their
+// first use. Per tile every wave runs one phase: the scores of tile i and,
+// between those MFMAs, the softmax and PV product of tile i-1; then the mask
+// and row max of tile i. Each wave waits for its own loads before the one
+// workgroup barrier per tile that hands the buffers over. The query rows of
+// the next piece are copied into LDS while the current one is computed.
 #include <atomic>
 #include <mutex>
 #include <type_traits>
@@ -55,11 +54,7 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-#ifndef TT_ATTN_PREFETCH
-#define TT_ATTN_PREFETCH 2
-#endif
-constexpr int kWaves = 8;                  // two groups of four waves, 32 query rows each
-constexpr int kNR = TT_ATTN_PREFETCH;      // tiles in flight in registers per wave (1 or 2)
+constexpr int kWaves = 8;       // 32 query rows each; waves 0-3 load K, waves 4-7 load V
 constexpr int kThreads = 64 * kWaves;
 constexpr int kFinThreads = 256;
 constexpr float kTau = 8.0f;  // lazy rescale threshold (log2 units)
@@ -71,24 +66,30 @@ template <int D>
 struct Cfg {
     static constexpr int CPR = D / 8;           // 16-byte chunks per K/V row
     static constexpr int ROWB = D * 2;          // bytes of one K/V row
-    static constexpr int KROW = ROWB + 16;      // LDS row pitch of K tiles
-    static constexpr int VROW = ROWB + 64;      // LDS row pitch of V tiles
-    static constexpr int KTILE = kTile * KROW;  // LDS bytes of one K tile
-    static constexpr int VTILE = kTile * VROW;  // LDS bytes of one V tile
-    static constexpr int RPI = 64 / CPR;        // rows one load instruction of a wave covers
+    static constexpr int TILEB = kTile * ROWB;  // LDS bytes of one K or V tile
+    static constexpr int RPI = 64 / CPR;        // rows one 1 KB load instruction covers
     static constexpr int LPG = 16 / RPI;        // load instructions per wave and tile (16 keys)
     static constexpr int DS = D / 16;           // k-steps of the score product
     static constexpr int DT = D / 32;           // d tiles of the output product
-    static_assert(LPG >= 1 && LPG <= 4, "");
+    static constexpr int KSH = CPR == 16 ? 0 : 1;  // K swizzle: log2(rows per 256-byte bank period)
+    static constexpr int G = CPR / 4;              // 64-byte groups per row
+    static constexpr int VSH = G == 4 ? 0 : 1;     // V swizzle: log2(rows per bank period / 4 * G)
+    static_assert((LPG == 2 || LPG == 4) && RPI * ROWB == 1024, "");
 };
 
-// LDS tiles keep the [key][d] layout with padded rows. A score-operand read
-// (ds_read_b128) has 16 lanes read one 16-byte chunk of 16 consecutive rows:
-// with a 272-byte K pitch (68 banks) those land on 16 disjoint 4-bank groups.
-// A transposing V read (ds_read_b64_tr_b16) has 32 lanes read 64 contiguous
-// bytes of each of 4 consecutive rows: with a 320-byte V pitch (80 banks)
-// those are 4 disjoint 16-bank groups. The padding keeps every address a
-// per-lane base plus a compile-time offset.
+// LDS tiles keep the [key][d] layout in unpadded rows with XOR swizzles, so a
+// direct-to-LDS load (each lane's 16 bytes land at 16 * lane) fills 1 KB of
+// rows at once. A score-operand read (ds_read_b128) has 16 lanes read one
+// 16-byte chunk c of 16 consecutive rows: chunk c of row r sits at position
+// c ^ kswz(r), so the 16 lanes hit the 16 distinct 16-byte slots of a
+// 256-byte bank period. A transposing V read (ds_read_b64_tr_b16) has 32 lanes
+// read one 64-byte group of 4 consecutive rows: group g of row r sits at
+// g ^ vswz(r), 4 distinct 64-byte slots. The loads put each lane's global
+// chunk where the swizzle wants it.
+template <int D>
+__device__ __forceinline__ int kswz(int r) { return (r >> Cfg<D>::KSH) & (Cfg<D>::CPR - 1); }
+template <int D>
+__device__ __forceinline__ int vswz(int r) { return (r >> Cfg<D>::VSH) & (Cfg<D>::G - 1); }
 
 // Element strides are 32-bit here (the host layer checks that they fit), which
 // keeps the kernel's scalar state small.
@@ -245,73 +246,12 @@ __device__ __forceinline__ int slot_of(const Args& a, int j) {
     return P2 ? (j & (a.page_size - 1)) : j % a.page_size;
 }
 
-// ---- tile staging: global -> registers -> LDS ------------------------------
-// Wave w (0..3 within its group) moves keys 16w .. 16w+15 of its group's half
-// tile: load instruction i covers rows 16w + RPI*i + lane/CPR, 16-byte chunk
-// lane%CPR. Sixteen 16-aligned keys lie in one page, so one page id serves the
-// wave for the whole tile.
-template <int D>
-struct Regs {
-    u32x4 x[Cfg<D>::LPG];
-};
-
-// Issue this wave's loads of tile c: keys 16*wq .. 16*wq+15 of the tile, load
-// instruction i covering rows RPI*i + lane/CPR of them (16-byte chunk
-// lane%CPR). The 16 keys lie in one page (page_size is a multiple of 16), so a
-// block of the prefix is a uniform base plus the lane's fixed offset `loff`.
-// Only a block that reaches past the prefix end clamps its rows to the last key
-// (finite data, weight exactly 0); a block wholly past the end reads the block
-// holding the last key. A page id outside [0, num_pages) is clamped, so a
-// corrupt table reads wrong data but never faults. Loads are unconditional and
-// their registers are not touched until they are stored to LDS.
-template <int D, bool P2>
-__device__ __forceinline__ void load_tile(Regs<D>& r, const Cur& c, int page, const uint16_t* src_c,
-                                          const uint16_t* src_d, const Args& a, int wq, int lane, unsigned loff) {
-    using C = Cfg<D>;
-    const int ch = lane % C::CPR, lrow = lane / C::CPR;
-    const char* base;
-    unsigned off[C::LPG];
-    if (TT_LIKELY(is_prefix(c, a))) {
-        int j0 = c.t * kTile + 16 * wq;
-        if (TT_UNLIKELY(j0 >= c.L)) j0 = (c.L - 1) & ~15;
-        const int last = c.L - 1 - j0;  // rows 0..last of the block are keys
-        page = min(max(page, 0), a.num_pages - 1);
-        base = reinterpret_cast<const char*>(src_c + (((long long)page * a.Hkv + c.g) * a.page_size +
-                                                      slot_of<P2>(a, j0)) * D);
-        if (TT_LIKELY(last >= 15)) {
-#pragma unroll
-            for (int i = 0; i < C::LPG; ++i) off[i] = loff + (unsigned)(C::RPI * i * D * 2);
-        } else {
-#pragma unroll
-            for (int i = 0; i < C::LPG; ++i) off[i] = (unsigned)((min(C::RPI * i + lrow, last) * D + ch * 8) * 2);
-        }
-    } else {
-        base = reinterpret_cast<const char*>(src_d + (long long)c.b * a.dsb + (long long)c.g * a.dsh);
-#pragma unroll
-        for (int i = 0; i < C::LPG; ++i)
-            off[i] = (unsigned)((min(16 * wq + C::RPI * i + lrow, a.S - 1) * a.dss + ch * 8) * 2);
-    }
-#pragma unroll
-    for (int i = 0; i < C::LPG; ++i)
-        r.x[i] = *reinterpret_cast<const u32x4*>(base + off[i]);
-}
-
-// registers -> LDS half tile with row pitch `pitch`
-template <int D>
-__device__ __forceinline__ void store_tile(const Regs<D>& r, uint8_t* buf, int pitch, int wq, int lane) {
-    using C = Cfg<D>;
-    uint8_t* p = buf + (16 * wq + lane / C::CPR) * pitch + 16 * (lane % C::CPR);
-#pragma unroll
-    for (int i = 0; i < C::LPG; ++i) *reinterpret_cast<u32x4*>(p + C::RPI * i * pitch) = r.x[i];
-}
-
 // Workgroup barrier ordering LDS accesses only: waits for this wave's own LDS
-// reads and writes (lgkmcnt), not for the global loads in flight. A
-// __syncthreads() or a workgroup fence would also wait for every global load,
-// since direct-to-LDS loads may be pending, and drain the prefetch; the data
-// those loads bring is waited for where it is read (each wave reads only its
-// own). The empty asm statements keep the compiler from moving memory
-// accesses across, the scheduling barriers every other instruction.
+// reads and writes (lgkmcnt), not for the global loads in flight. The callers
+// wait for the direct-to-LDS loads whose data other waves read next
+// (vmcnt) just before it. The empty asm statements keep the compiler from
+// moving memory accesses across, the scheduling barriers every other
+// instruction.
 __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
@@ -413,22 +353,93 @@ __device__ __forceinline__ void lds_write_b64(unsigned addr, unsigned lo, unsign
     asm volatile("ds_write_b64 %0, %1" : : "v"(addr), "v"(v) : "memory");
 }
 
+// ---- tile staging: global -> LDS ------------------------------------------
+// Wave wq (0..3 within its group) moves keys 16 wq .. 16 wq + 15 of its
+// group's half tile with LPG direct-to-LDS buffer loads of 1 KB: load k
+// writes tile rows 16 wq + RPI k + lane / CPR, the lane's 16 bytes at slot
+// lane % CPR of the row, which holds global chunk (lane % CPR) ^ swizzle.
+// Sixteen 16-aligned keys lie in one page, so one page id serves the wave for
+// the whole tile, and a full block reads 16 contiguous rows of that page.
+// goff[k] is the lane's byte offset for load k of a full block; load k writes
+// LDS from lbuf + (16 wq + RPI k) * ROWB = lbuf + 16 wq * ROWB + 1024 k.
+template <int D>
+__device__ __forceinline__ unsigned stage_chunk(bool v_half, int r, int p) {
+    return v_half ? (unsigned)(p ^ (vswz<D>(r) << 2)) : (unsigned)(p ^ kswz<D>(r));
+}
+
+// Issue this wave's loads of tile c into LDS buffer `lbuf`. The prefix block is
+// read through a buffer resource covering its 16 rows only. A block that
+// reaches past the prefix end reads its last key again in the rows beyond it
+// (finite data, weight exactly 0); a block wholly past the end reads the block
+// holding the last key. A page id outside [0, num_pages) is clamped, so a
+// corrupt table reads wrong data but never faults.
+template <int D, bool P2>
+__device__ __forceinline__ void dma_tile(uint8_t* lbuf, const Cur& c, int page, const uint16_t* src_c,
+                                         const uint16_t* src_d, const Args& a, bool v_half, int wq,
+                                         const unsigned (&goff)[Cfg<D>::LPG]) {
+    using C = Cfg<D>;
+    __amdgpu_buffer_rsrc_t rs;
+    unsigned off[C::LPG];
+    if (TT_LIKELY(is_prefix(c, a))) {
+        int j0 = c.t * kTile + 16 * wq;
+        if (TT_UNLIKELY(j0 >= c.L)) j0 = (c.L - 1) & ~15;
+        const int last = c.L - 1 - j0;  // rows 0..last of the block are keys
+        page = min(max(page, 0), a.num_pages - 1);
+        const uint16_t* base = src_c + (((long long)page * a.Hkv + c.g) * a.page_size + slot_of<P2>(a, j0)) * D;
+        rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 16 * C::ROWB, 0x00020000);
+        if (TT_LIKELY(last >= 15)) {
+#pragma unroll
+            for (int k = 0; k < C::LPG; ++k) off[k] = goff[k];
+        } else {
+            const unsigned ln = lane_here();
+#pragma unroll
+            for (int k = 0; k < C::LPG; ++k) {
+                const int rr = C::RPI * k + (int)(ln / C::CPR);
+                off[k] = (unsigned)(min(rr, last) * C::ROWB) + 16u * stage_chunk<D>(v_half, rr, (int)(ln % C::CPR));
+            }
+        }
+    } else {
+        const uint16_t* base = src_d + (long long)c.b * a.dsb + (long long)c.g * a.dsh;
+        rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7FFFFFFF, 0x00020000);
+        const unsigned ln = lane_here();
+#pragma unroll
+        for (int k = 0; k < C::LPG; ++k) {
+            const int rr = C::RPI * k + (int)(ln / C::CPR);
+            off[k] = (unsigned)(min(16 * wq + rr, a.S - 1) * a.dss * 2) +
+                     16u * stage_chunk<D>(v_half, rr, (int)(ln % C::CPR));
+        }
+    }
+    uint8_t* const dst = lbuf + 16 * wq * C::ROWB;
+#pragma unroll
+    for (int k = 0; k < C::LPG; ++k)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + 1024 * k), 16,
+                                                 off[k], 0, 0, 0);
+}
+
 template <int D, bool P2>
 __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const int* __restrict__ page_table,
                                                                 const int* __restrict__ ctx_len) {
     using C = Cfg<D>;
-    // K tiles (two buffers), then V tiles (two buffers)
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * C::KTILE + 2 * C::VTILE];
+    // K and V tiles, two buffers each (tile j in buffer j % 2). Separate
+    // arrays, so that the compiler tells the buffers apart when it places the
+    // waits for the direct-to-LDS loads before its own LDS reads.
+    __shared__ __attribute__((aligned(1024))) uint8_t kb0[C::TILEB];
+    __shared__ __attribute__((aligned(1024))) uint8_t kb1[C::TILEB];
+    __shared__ __attribute__((aligned(1024))) uint8_t vb0[C::TILEB];
+    __shared__ __attribute__((aligned(1024))) uint8_t vb1[C::TILEB];
     __shared__ int pgs[kWaves][2][64];  // page-id batches of each wave
     // Query rows of the next piece, fetched ahead: wave w's 32 rows, lane l's
     // 16 bytes of k-step ds at [w][1024 ds + 16 l]. Between pieces the same
     // bytes stage a finished piece's bf16 rows (32 rows of pitch ROWB + 16).
     __shared__ __attribute__((aligned(16))) uint8_t qlds[kWaves][C::DS * 1024 + 512];
+    uint8_t* const KR[2] = {kb0, kb1};
+    uint8_t* const VR[2] = {vb0, vb1};
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int grp = wave >> 2, wq = wave & 3;
+    const int wq = wave & 3;
+    const bool vh = wave >= 4;  // this wave loads the V half of every tile
     const int l32 = lane & 31, hl = lane >> 5;
 
     // logical segment of this workgroup: consecutive segments share an XCD
@@ -454,14 +465,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
     cc.t = t0;
     const int mult = a.Hkv * a.n_rb;
 
-    // ---- this group's half of every tile ----
-    const uint16_t* src_c = grp ? a.Vc : a.Kc;
-    const uint16_t* src_d = grp ? a.Vd : a.Kd;
-    const uint8_t* const Kbuf = smem;
-    const uint8_t* const Vbuf = smem + 2 * C::KTILE;
-    uint8_t* const mybuf = smem + (grp ? 2 * C::KTILE : 0);
-    const int mypitch = grp ? C::VROW : C::KROW;
-    const int mytile = grp ? C::VTILE : C::KTILE;
+    // ---- this wave's half of every tile ----
+    const uint16_t* src_c = vh ? a.Vc : a.Kc;
+    const uint16_t* src_d = vh ? a.Vd : a.Kd;
+    // this lane's byte offsets for the loads of a full 16-key block
+    unsigned goff[C::LPG];
+#pragma unroll
+    for (int k = 0; k < C::LPG; ++k)
+        goff[k] = (unsigned)((C::RPI * k + lane / C::CPR) * C::ROWB) +
+                  16u * stage_chunk<D>(vh, C::RPI * k + lane / C::CPR, lane % C::CPR);
     // page ids through a bounds-checked buffer resource (an empty table reads 0)
     const __amdgpu_buffer_rsrc_t ptab = __builtin_amdgcn_make_buffer_rsrc(
         (void*)page_table, (short)0, page_table ? a.B * a.max_pages * 4 : 0, 0x00020000);
@@ -471,10 +483,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
     // ahead + l tiles (across pair and sequence boundaries) and fetches the
     // page of its 16 keys with one direct-to-LDS buffer load for the batch. A
     // batch is fetched when the one before it comes into use, 64 tiles ahead
-    // of its own first use, after that tile's id is read: the wait for it is
-    // then never more than the wait for the tile loads issued before it (the
-    // in-order load counter reports a page-table read only together with
-    // every load before it).
+    // of its own first use.
     auto page_batch = [&](const Cur& c, int first, int ahead, int buf) __attribute__((always_inline)) {
         int idx = 0;
         if (lane + ahead < n - first) {  // tiles past the segment stay at index 0
@@ -498,8 +507,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
 
     // Direct-to-LDS copy of the query rows of the piece at c (the fragments
     // load_q would read, each lane's 16 bytes of step ds at qlds[wave][1024 ds +
-    // 16 lane]). It is issued when the load cursor enters the piece, kNR + 1
-    // tiles before the piece is computed, if the buffer is free.
+    // 16 lane]). It is issued when the load cursor enters the piece, if the
+    // buffer is free.
     auto q_dma = [&](const Cur& c) __attribute__((always_inline)) {
         const unsigned ln = lane_here();
         const int rb = c.pl - c.g * a.n_rb;
@@ -515,12 +524,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
     };
     int q_tag = -1;  // segment index of the piece start whose rows are in qlds (-1: none)
 
-    // Load pipeline: tile j's registers are filled kNR tiles before they are
-    // stored. Every issue loads a whole tile (past the segment's end it reloads
-    // the last one), so the wait counts the compiler derives are exact and
-    // never drain the pipeline.
-    Regs<D> R[kNR];
-    const unsigned loff = (unsigned)(((lane / C::CPR) * D + (lane % C::CPR) * 8) * 2);  // byte offset in a block
+    // Load pipeline: the K waves request tile i+1 and the V waves tile i at
+    // the start of tile i's phase (V is used one tile later than K), and every
+    // wave waits for its own loads before the barrier that ends the phase.
+    // Every issue loads a whole tile (past the segment's end it reloads the
+    // last one).
     Cur cl = cc;  // next tile to load
     int ul = 0;   // its index in the segment
     int pg_base = 0;
@@ -531,7 +539,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
     page_batch(cl, 0, 64, 1);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): both batches have landed
     int pgl = pgs[wave][0][lane];
-    auto issue = [&](Regs<D>& r) __attribute__((always_inline)) {
+    auto issue = [&](uint8_t* lbuf) __attribute__((always_inline)) {
         if (TT_UNLIKELY(ul - pg_base == 64)) {
             pg_base = ul;
             pbuf ^= 1;
@@ -542,7 +550,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
         const int page = __builtin_amdgcn_readlane(pgl, ul - pg_base);
         if (TT_UNLIKELY(a.dbg != nullptr) && is_prefix(cl, a) && (page < 0 || page >= a.num_pages) && lane == 0)
             atomicOr(a.dbg, TT_DEBUG_PAGE_ID);
-        load_tile<D, P2>(r, cl, page, src_c, src_d, a, wq, lane, loff);
+        dma_tile<D, P2>(lbuf, cl, page, src_c, src_d, a, vh, wq, goff);
         if (ul + 1 < n) {
             advance(cl, a, ctx_len);
             ++ul;
@@ -552,16 +560,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
             }
         }
     };
-    // Tile j's registers are R[j % kNR]: stored to LDS buffer j % 2, then
-    // refilled with tile j + kNR.
-    auto store = [&](auto J_, int j) __attribute__((always_inline)) {
-        constexpr int J = decltype(J_)::value;  // j % 2
-        if (TT_LIKELY(j < n)) store_tile<D>(R[J % kNR], mybuf + J * mytile, mypitch, wq, lane);
-    };
-    auto feed = [&](auto J_, int j) __attribute__((always_inline)) {
-        store(J_, j);
-        issue(R[decltype(J_)::value % kNR]);
-    };
 
     // ---- per-wave state ----
     bf16x8 qf[C::DS];
@@ -570,12 +568,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
     bf16x8 pf[4];
     float m2 = -INFINITY, lsum = 0.f;
     int piece_t0 = 0;
-    // lane parts of the LDS operand addresses: score reads take chunk
-    // 2*ds + hl of row l32 (+32 mt); V reads take bytes vbyte.. of chunk
-    // 4*dt + vchunk of row vrow (+16 ks, +8 for the second half)
-    const int kaddr = l32 * C::KROW + 16 * hl;
-    const int vaddr = (4 * hl + ((lane & 15) >> 2)) * C::VROW + 16 * (2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) +
-                      8 * (lane & 1);
+    // lane parts of the LDS operand addresses. Score reads take chunk 2 cc + hl
+    // of row l32 (+32 mt): kad[cc]. V reads take bytes 64 dt + vin of row vr
+    // (+16 ks, +8 for the second half): vad[dt]. The swizzles of rows l32 + 32 mt
+    // and vr + 16 ks + 8 are those of l32 and vr.
+    unsigned kad[C::DS], vad[C::DT];
+#pragma unroll
+    for (int c2 = 0; c2 < C::DS; ++c2) kad[c2] = l32 * C::ROWB + 16 * ((2 * c2 + hl) ^ kswz<D>(l32));
+    {
+        const int vr = 4 * hl + ((lane & 15) >> 2);
+        const int vin = 16 * (2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) + 8 * (lane & 1);
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) vad[dt] = vr * C::ROWB + 64 * (dt ^ vswz<D>(vr)) + vin;
+    }
 
     // query rows of the pair at c (a row past S*G reads the last row; it is never written)
     auto load_q = [&](const Cur& c) __attribute__((always_inline)) {
@@ -589,11 +594,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
         for (int ds = 0; ds < C::DS; ++ds) qf[ds] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q + ds * 16));
     };
 
-    // matrix phase of tile j: S^T of tile j from K buffer KB = j % 2 into
+    // matrix part of tile j: S^T of tile j from K buffer KB = j % 2 into
     // sacc[KB] (if QK); the softmax of tile j-1 (scores sacc[VB], running max
-    // from the vector phase before) and O^T += V^T P^T for it from V buffer
-    // VB = (j-1) % 2 (if PV). Per 16-key step ks: the operands of step ks+1
-    // are read from LDS while the step's MFMAs run, and the softmax of keys
+    // from the tile before) and O^T += V^T P^T for it from V buffer VB =
+    // (j-1) % 2 (if PV). Per 16-key step ks: the operands of step ks+1 are
+    // read from LDS while the step's MFMAs run, and the softmax of keys
     // 16ks .. 16ks+15 (P^T fragment pf[ks]) fills the vector ALU meanwhile.
     // The score product runs K-row half outer (steps 0-1 rows 0-31, steps 2-3
     // rows 32-63), so the new tile's second half comes alive as the old
@@ -607,14 +612,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
         constexpr bool QK = decltype(QK_)::value;
         constexpr bool PV = decltype(PV_)::value;
         constexpr int KB = decltype(KB_)::value, VB = decltype(VB_)::value;
-        const uint8_t* Kst = Kbuf + KB * C::KTILE + kaddr;
-        const uint8_t* Vst = Vbuf + VB * C::VTILE + vaddr;
+        const uint8_t* Kst = KR[KB];
+        const uint8_t* Vst = VR[VB];
         auto read = [&](Frag& f, auto KS_) __attribute__((always_inline)) {
             constexpr int ks = decltype(KS_)::value;
             if constexpr (QK) {
 #pragma unroll
                 for (int dd = 0; dd < DPS; ++dd)
-                    f.k[dd] = lds16(Kst + (ks / 2) * 32 * C::KROW + 32 * ((ks % 2) * DPS + dd));
+                    f.k[dd] = lds16(Kst + kad[(ks % 2) * DPS + dd] + (ks / 2) * 32 * C::ROWB);
             }
             if constexpr (PV) {
                 // V sits in LDS as [key][d]; the transposing read hands lane l the four keys
@@ -622,8 +627,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
                 // exactly the keys its P^T slots hold.
 #pragma unroll
                 for (int dt = 0; dt < C::DT; ++dt) {
-                    const uint8_t* p0 = Vst + ks * 16 * C::VROW + 64 * dt;
-                    const i16x4 pair[2] = {lds_tr(p0), lds_tr(p0 + 8 * C::VROW)};
+                    const uint8_t* p0 = Vst + vad[dt] + ks * 16 * C::ROWB;
+                    const i16x4 pair[2] = {lds_tr(p0), lds_tr(p0 + 8 * C::ROWB)};
                     f.v[dt] = __builtin_bit_cast(bf16x8, pair);
                 }
             }
@@ -662,7 +667,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
                 __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // LDS read
             }
         };
-        __builtin_amdgcn_s_setprio(1);
         using I0 = std::integral_constant<int, 0>;
         using I1 = std::integral_constant<int, 1>;
         using I2 = std::integral_constant<int, 2>;
@@ -673,7 +677,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
         step(f0, I0{});
         __builtin_amdgcn_sched_barrier(0);
         // in the two middle regions, pairs of MFMAs alternate with groups of three
-        // LDS reads (measured 2-4% faster than the compiler's own order)
+        // LDS reads
         read(f0, I2{});
         step(f1, I1{});
         interleave();
@@ -797,16 +801,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
     // the piece of tile i - 1, if that tile ended its pair
     bool prev_ends = false;
     int prev_b = 0, prev_pl = 0, prev_g = 0;
-    // vector phase of tile i: close the piece that ended with tile i-1 (its last
-    // softmax and PV product ran in this tile's matrix phase), mask and row max
+    // vector part of tile i: close the piece that ended with tile i-1 (its last
+    // softmax and PV product ran in this tile's matrix part), mask and row max
     // of tile i (the rescale it may call for applies before tile i's weights
-    // are added, in the next matrix phase), stage tile i+1
+    // are added, in the next matrix part), move to tile i+1
     auto vector = [&](auto P_, int i) __attribute__((always_inline)) {
         constexpr int P = decltype(P_)::value;  // i % 2
-        __builtin_amdgcn_s_setprio(0);
-        // my half of tile i+1 into LDS first: the writes complete while the
-        // rest of the phase runs (its buffer was last read two intervals ago)
-        store(std::integral_constant<int, 1 - P>{}, i + 1);
         const bool close_prev = i > 0 && prev_ends;
         if (TT_UNLIKELY(close_prev)) epilogue(prev_b, prev_pl, prev_g, piece_t0 == 0);
         if (TT_UNLIKELY(i == 0 || close_prev)) {
@@ -844,9 +844,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
 #pragma unroll
                 for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
         }
-        // next tile: its query rows if it starts a new piece (issued before the
-        // staging loads, so waiting for them leaves those in flight), then the
-        // loads of tile i+1+kNR
+        // next tile: its query rows if it starts a new piece
         prev_ends = cc.t == cc.units - 1;
         prev_b = cc.b;
         prev_pl = cc.pl;
@@ -855,69 +853,62 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
             advance(cc, a, ctx_len);
             if (TT_UNLIKELY(cc.t == 0)) {
                 if (q_tag == i + 1) {
-                    // the copy was issued before the loads of tile i+1, which were
-                    // waited for when that tile was staged at the start of this
-                    // phase, and loads complete in order
+                    // the copy may still be in flight (a V wave issues it in this tile)
+                    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
                     read_q_lds(qf, (unsigned)(uintptr_t)&qlds[wave][0]);
                     q_tag = -1;
                 } else {
-                    // waited for here, once per piece: left pending, the wait
-                    // would sit before every tile's score MFMAs
                     load_q(cc);
                     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
                 }
             }
         }
-        issue(R[(1 - P) % kNR]);
     };
 
-    // ---- prologue: the loads of the first tile, the query rows, the loads of
-    // the tiles after (so the rows arrive with the first tile); group 0 stages
-    // K of tile 0 before the first barrier, group 1 stages V of tile 0 in the
-    // first interval ----
-    issue(R[0]);
-    load_q(cc);
-#pragma unroll
-    for (int k = 1; k < kNR; ++k) issue(R[k]);
-    if (grp == 0) feed(std::integral_constant<int, 0>{}, 0);
-    lds_barrier();
-    if (grp == 1) {
-        feed(std::integral_constant<int, 0>{}, 0);
-        lds_barrier();
-    }
+    // One phase per tile i: the loads (K of tile i+1, V of tile i), the matrix
+    // part (scores of i, softmax and PV of i-1), the vector part, then this
+    // wave's loads are waited for and the barrier hands the buffers over.
     using F = std::false_type;
     using T = std::true_type;
     using Z = std::integral_constant<int, 0>;
     using O = std::integral_constant<int, 1>;
-    // Tile i: matrix(i) = scores of i (K buffer i%2) and PV of i-1 (V buffer
-    // (i-1)%2), then vector(i). The loop runs from one vector phase to the next.
-    matrix(T{}, F{}, Z{}, Z{});
+    auto tile = [&](auto J_, int i) __attribute__((always_inline)) {
+        constexpr int J = decltype(J_)::value;  // i % 2
+        using JC = std::integral_constant<int, J>;
+        using JP = std::integral_constant<int, 1 - J>;
+        issue(vh ? VR[J] : KR[1 - J]);
+        matrix(T{}, T{}, JC{}, JP{});
+        vector(JC{}, i);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's part of tile i+1 (K) / i (V)
+        lds_barrier();
+    };
+
+    // ---- prologue: K of tile 0 and the query rows of the first piece ----
+    if (!vh) issue(KR[0]);
+    load_q(cc);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     lds_barrier();
-    int i = 0;
-    for (; i + 2 < n; i += 2) {
-        vector(Z{}, i);
-        lds_barrier();
-        matrix(T{}, T{}, O{}, Z{});
-        lds_barrier();
-        vector(O{}, i + 1);
-        lds_barrier();
-        matrix(T{}, T{}, Z{}, O{});
-        lds_barrier();
-    }
-    vector(Z{}, i);
+    // tile 0: no PV product yet
+    issue(vh ? VR[0] : KR[1]);
+    matrix(T{}, F{}, Z{}, O{});
+    vector(Z{}, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     lds_barrier();
-    if (i + 1 < n) {
-        matrix(T{}, T{}, O{}, Z{});
-        lds_barrier();
-        vector(O{}, i + 1);
-        lds_barrier();
-        matrix(F{}, T{}, Z{}, O{});  // PV of the last tile (odd)
-    } else {
-        matrix(F{}, T{}, Z{}, Z{});  // PV of the last tile (even)
+    int i = 1;
+    for (; i + 1 < n; i += 2) {
+        tile(O{}, i);
+        tile(Z{}, i + 1);
     }
-    __builtin_amdgcn_s_setprio(0);
+    if (i < n) {
+        tile(O{}, i);
+        ++i;
+    }
+    // PV of the last tile, n - 1
+    if ((n - 1) % 2 == 0)
+        matrix(F{}, T{}, Z{}, Z{});
+    else
+        matrix(F{}, T{}, Z{}, O{});
     epilogue(cc.b, cc.pl, cc.g, piece_t0 == 0 && cc.t == cc.units - 1);
-    if (grp == 0) lds_barrier();
 }
 
 // Merge the per-segment partials of every pair that segment boundaries cut,

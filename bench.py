@@ -180,8 +180,11 @@ def oracle_attn_time(d, rows=None, threads=None):
 
 
 def host_threads():
+    """Threads for the oracle's all-threads figure: the process's CPU share (OMP_NUM_THREADS when
+    the environment sets it, else the CPUs this process may run on)."""
     import oracle
-    oracle.set_num_threads(max(1, len(os.sched_getaffinity(0))))
+    n = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    oracle.set_num_threads(max(1, n))
     return oracle.num_threads()
 
 
