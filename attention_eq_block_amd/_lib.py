@@ -10,7 +10,8 @@ import os
 import re
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libtwotower_attn.so")
+# TT_LIBRARY selects another build of the library (the sanitizer test loads one)
+LIB_PATH = os.environ.get("TT_LIBRARY") or os.path.join(PKG, "libtwotower_attn.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "twotower_attn.h")
 
 TT_F32, TT_BF16 = 0, 1

@@ -49,14 +49,15 @@ def _run(cmd):
         print(err, file=sys.stderr)
 
 
-def build(out: str = LIB, jobs: int = 0) -> str:
-    """Compile every source to an object in parallel, then link the shared library."""
+def build(out: str = LIB, jobs: int = 0, extra=(), link_extra=()) -> str:
+    """Compile every source to an object in parallel, then link the shared library. ``extra`` adds
+    compiler flags (the sanitizer test builds a host-instrumented copy elsewhere with it)."""
     with tempfile.TemporaryDirectory(prefix="tt_build_") as tmp:
         objs, procs = [], []
         for src in SOURCES:
             obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
             lang = ["-x", "hip"] if src.endswith(".hip") else ["-x", "hip"]
-            cmd = [HIPCC, *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [HIPCC, *COMMON, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
             procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
             objs.append(obj)
         failed = []
@@ -71,7 +72,7 @@ def build(out: str = LIB, jobs: int = 0) -> str:
         if failed:
             raise RuntimeError("HIP build failed:\n" + "\n\n".join(failed))
         tmp_out = out + ".tmp"
-        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_out])
+        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_extra, *objs, "-o", tmp_out])
         os.replace(tmp_out, out)
     return out
 

@@ -3,6 +3,7 @@
 #include <math.h>
 #include <stdio.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include <atomic>
 
@@ -28,6 +29,16 @@ int device_cu_count() {
 bool log_enabled() {
     static const bool on = [] {
         const char* v = getenv("TT_LOG");
+        return v && v[0] && v[0] != '0';
+    }();
+    return on;
+}
+
+// Fault injection for tests of the error path: with TT_INJECT_HIP_ERROR set (and not "0"),
+// every entry point that would launch returns TT_ERR_HIP after validation, launching nothing.
+bool inject_hip_error() {
+    static const bool on = [] {
+        const char* v = getenv("TT_INJECT_HIP_ERROR");
         return v && v[0] && v[0] != '0';
     }();
     return on;
@@ -144,7 +155,10 @@ extern "C" {
 
 int tt_abi_version(void) { return TT_ABI_VERSION; }
 
-const char* tt_status_string(tt_status s) {
+const char* tt_status_string(tt_status status) {
+    // a C caller may pass any int: read the bits, not a (possibly out-of-range) enum value
+    int32_t s;
+    memcpy(&s, &status, sizeof s);
     switch (s) {
         case TT_OK: return "TT_OK: success";
         case TT_ERR_NULL: return "TT_ERR_NULL: a required pointer is NULL";
@@ -171,11 +185,12 @@ tt_status tt_block_attn(const tt_block_attn_params* p, void* workspace, size_t w
             if (log_enabled())
                 fprintf(stderr, "[tt] block_attn f32 B=%d S=%d Hq=%d Hkv=%d d=%d Lmax=%d\n", p->B, p->S, p->Hq,
                         p->Hkv, p->head_dim, p->max_ctx_len);
-            return tt::launch_attn_f32(*p, stream);
+            return inject_hip_error() ? TT_ERR_HIP : tt::launch_attn_f32(*p, stream);
         }
         const tt::AttnPlan plan = tt::plan_attn_bf16(*p, device_cu_count());
         if (ws_bytes < plan.ws_total || workspace == nullptr) return TT_ERR_WORKSPACE;
         if (!aligned16(workspace)) return TT_ERR_UNSUPPORTED;
+        if (inject_hip_error()) return TT_ERR_HIP;
         if (log_enabled())
             fprintf(stderr, "[tt] block_attn bf16 B=%d S=%d Hq=%d Hkv=%d d=%d Lmax=%d seg=%d pairs=%d ws=%zu\n",
                     p->B, p->S, p->Hq, p->Hkv, p->head_dim, p->max_ctx_len, plan.n_seg, plan.n_pairs,
@@ -190,7 +205,7 @@ tt_status tt_block_attn_noalloc(const tt_block_attn_params* p, hipStream_t strea
     const tt_status v = validate_attn(p);
     if (v != TT_OK || p->B == 0) return v;
     try {
-        if (p->dtype == TT_F32) return tt::launch_attn_f32(*p, stream);  // needs no scratch
+        if (p->dtype == TT_F32) return inject_hip_error() ? TT_ERR_HIP : tt::launch_attn_f32(*p, stream);
         const tt::AttnPlan plan = tt::plan_attn_bf16(*p, device_cu_count());
         if (plan.ws_total > tt::kNoallocScratchBytes) {
             if (log_enabled())
@@ -198,6 +213,7 @@ tt_status tt_block_attn_noalloc(const tt_block_attn_params* p, hipStream_t strea
                         plan.ws_total, tt::kNoallocScratchBytes);
             return TT_ERR_WORKSPACE;
         }
+        if (inject_hip_error()) return TT_ERR_HIP;
         tt_status st = TT_OK;
         void* ws = tt::noalloc_scratch(&st);
         if (!ws) return st;
@@ -211,7 +227,10 @@ tt_status tt_block_attn_noalloc(const tt_block_attn_params* p, hipStream_t strea
 }
 
 tt_status tt_lse_merge(int P, const float* O_parts, const float* lse_parts, int B, int S, int Hq, int d,
-                       void* O_out, tt_dtype o_dtype, float* lse_out, hipStream_t stream) {
+                       void* O_out, tt_dtype o_dtype_arg, float* lse_out, hipStream_t stream) {
+    // a C caller may pass any int: read the bits, not a (possibly out-of-range) enum value
+    int32_t o_dtype;
+    memcpy(&o_dtype, &o_dtype_arg, sizeof o_dtype);
     if (P < 1 || B < 0 || S < 1 || Hq < 1 || d < 4 || d % 4 != 0) return TT_ERR_SHAPE;
     if (o_dtype != TT_F32 && o_dtype != TT_BF16) return TT_ERR_DTYPE;
     if (B == 0) return TT_OK;
@@ -219,6 +238,7 @@ tt_status tt_lse_merge(int P, const float* O_parts, const float* lse_parts, int 
     if (!aligned16(O_parts) || !aligned16(O_out)) return TT_ERR_UNSUPPORTED;
     if (o_dtype == TT_BF16 && d % 8 != 0) return TT_ERR_UNSUPPORTED;
     try {
+        if (inject_hip_error()) return TT_ERR_HIP;
         return tt::launch_lse_merge(P, O_parts, lse_parts, B, S, Hq, d, O_out, o_dtype, lse_out, stream);
     } catch (...) {
         return TT_ERR_HIP;
@@ -240,6 +260,7 @@ tt_status tt_conf_unmask(const tt_conf_unmask_params* p, void* workspace, size_t
         if (log_enabled())
             fprintf(stderr, "[tt] conf_unmask B=%d S=%d V=%d vsplit=%d gamma=%g T=%g R=%d\n", p->B, p->S, p->V,
                     plan.n_vsplit, p->gamma, p->temperature, p->steps_left);
+        if (inject_hip_error()) return TT_ERR_HIP;
         return tt::launch_unmask(*p, plan, workspace, stream);
     } catch (...) {
         return TT_ERR_HIP;
@@ -253,6 +274,7 @@ tt_status tt_kv_append(const tt_kv_append_params* p, hipStream_t stream) {
         if (log_enabled())
             fprintf(stderr, "[tt] kv_append B=%d S=%d Hkv=%d d=%d page=%d pages=%d\n", p->B, p->S, p->Hkv,
                     p->head_dim, p->page_size, p->num_pages);
+        if (inject_hip_error()) return TT_ERR_HIP;
         return tt::launch_kv_append(*p, stream);
     } catch (...) {
         return TT_ERR_HIP;
@@ -273,6 +295,7 @@ tt_status tt_masked_nll(const tt_masked_nll_params* p, void* workspace, size_t w
         if (!aligned16(workspace)) return TT_ERR_UNSUPPORTED;
         if (log_enabled())
             fprintf(stderr, "[tt] masked_nll B=%d S=%d V=%d vsplit=%d\n", p->B, p->S, p->V, plan.n_vsplit);
+        if (inject_hip_error()) return TT_ERR_HIP;
         return tt::launch_nll(*p, plan, workspace, stream);
     } catch (...) {
         return TT_ERR_HIP;

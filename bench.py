@@ -22,7 +22,7 @@ the CPU oracle on a bounded sample as a baseline.
 
 The default run (loop workload) also times the other four workloads and reports them in
 "per_config", one entry per workload: the tiny fp32 call and its unmask step (us), the
-single-layer call cold (a 512 MB buffer rewritten before each call) and warm, the ragged
+single-layer call cold (a 512 MB buffer read before each call) and warm, the ragged
 batch and its 64 x 16 x 131072 unmask step, and the long-prefix call against the bf16 MFMA
 roof; every entry has the median, p10 and p90 of at least 20 calls timed one by one and the
 oracle on a bounded sample at one thread and at every host thread. The loop itself also runs
@@ -84,7 +84,7 @@ def measured_traffic():
         return None
 METRIC = "noisy-block tokens/s per attn layer (S=16); achieved HBM TB/s vs peak"
 MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
-SCRUB_BYTES = 512 << 20    # written between timed calls so that the next one reads HBM, not the 256 MB MALL
+SCRUB_BYTES = 512 << 20    # read between timed calls so that the next one reads HBM, not the 256 MB MALL
 
 
 def log(*a):
@@ -107,15 +107,15 @@ def spread_us(ms):
 
 
 class Scrub:
-    """A 512 MB buffer rewritten between timed calls (outside their events)."""
+    """A 512 MB buffer read between timed calls (outside their events). Reading, not writing: a
+    write would leave dirty lines in the caches whose write-back the next timed call would pay."""
 
     def __init__(self):
-        self.buf = torch.empty(SCRUB_BYTES // 4, dtype=torch.float32, device="cuda")
-        self.k = 0
+        self.buf = torch.ones(SCRUB_BYTES // 4, dtype=torch.float32, device="cuda")
+        self.sink = torch.zeros((), dtype=torch.float32, device="cuda")
 
     def __call__(self):
-        self.k += 1
-        self.buf.fill_(float(self.k))
+        torch.sum(self.buf, dim=0, out=self.sink)
 
 
 def time_each(call, stream, reps, warmup, scrub=None):
@@ -263,7 +263,7 @@ def run_single(args, name, stream):
                                                                    else ""),
            "call_us": spread_us(ms), "tflops": case.flops() / (med * 1e-3) / 1e12,
            "roofline": attn_roofline(case, med, bound),
-           "timing": "per call between HIP events; a 512 MB buffer rewritten before each call"
+           "timing": "per call between HIP events; a 512 MB buffer read before each call"
            if name != "tiny" else "per call between HIP events"}
     if name == "tiny":
         res["roofline"] = {"bound": "latency", "note": "66 KB per call: launch latency, reported in us"}

@@ -22,7 +22,8 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libtt_oracle.so")
+# TT_ORACLE_LIBRARY selects another build of the oracle (the sanitizer test loads one)
+_LIB_PATH = os.environ.get("TT_ORACLE_LIBRARY") or os.path.join(_HERE, "libtt_oracle.so")
 _lib = None
 
 _P = ctypes.c_void_p
