@@ -1,8 +1,11 @@
 // Eq. (1) of Nemotron-TwoTower (arXiv 2606.26493, section 2.1) for float32
-// inputs: one wavefront per query row (b, s, h), lanes spread over head_dim,
-// keys visited in order (prefix tokens through the page table, then the S
-// block tokens) with an online softmax in float32. This path serves float32
-// callers and small shapes; the bf16 MFMA path is the throughput path.
+// inputs: one wavefront per query row (b, s, h). Keys are taken 64 at a time,
+// one per lane: each lane computes its key's score against the query row
+// (read from LDS as a broadcast), one wave reduction per 64 keys gives the
+// running max and sum (online softmax in float32), and the P.V product runs
+// with lanes over head_dim, each key's weight broadcast from its lane. This
+// path serves float32 callers and small shapes; the bf16 MFMA path is the
+// throughput path.
 #include "tt_internal.h"
 
 namespace tt {
@@ -32,14 +35,23 @@ __device__ __forceinline__ float wave_sum(float x) {
     for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
     return x;
 }
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+    return x;
+}
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <int D>
 __global__ __launch_bounds__(256) void attn_f32_kernel(F32Args a) {
-    constexpr int E = D / 64;  // elements of head_dim per lane
+    constexpr int E = D / 64;  // elements of head_dim per lane in the P.V product
+    __shared__ __attribute__((aligned(16))) float qs[4][D];
     const int lane = threadIdx.x & 63;
-    const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int w = threadIdx.x >> 6;
+    const long long row = (long long)blockIdx.x * 4 + w;
     const long long n_rows = (long long)a.B * a.S * a.Hq;
-    if (row >= n_rows) return;
+    if (row >= n_rows) return;  // whole waves only: no barrier below
     const int h = (int)(row % a.Hq);
     const int s = (int)((row / a.Hq) % a.S);
     const int b = (int)(row / ((long long)a.Hq * a.S));
@@ -51,19 +63,28 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(F32Args a) {
     }
     const int n = L + (a.Kd ? a.S : 0);
 
-    float q[E], o[E];
-    const float* qp = a.Q + b * a.qsb + s * a.qss + h * a.qsh + lane * E;
+    // the query row, in this wave's LDS slot (read back as broadcasts)
+    const float* qp = a.Q + b * a.qsb + s * a.qss + h * a.qsh;
 #pragma unroll
-    for (int e = 0; e < E; ++e) { q[e] = qp[e]; o[e] = 0.f; }
+    for (int e = 0; e < E; ++e) qs[w][lane * E + e] = qp[lane * E + e];
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    float o[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] = 0.f;
     float m = -INFINITY, l = 0.f;
-    for (int j = 0; j < n; ++j) {
+    for (int j0 = 0; j0 < n; j0 += 64) {
+        // this lane's key j (past the end: the last key again, weight 0)
+        const int j = min(j0 + lane, n - 1);
         const float* kp;
         const float* vp;
         if (j < L) {
             // a page id outside the pool is clamped into it (wrong data, no fault)
             int page = a.page_table[(long long)b * a.max_pages + j / a.page_size];
             if (page < 0 || page >= a.num_pages) {
-                if (a.dbg && lane == 0) atomicOr(a.dbg, TT_DEBUG_PAGE_ID);
+                if (a.dbg) atomicOr(a.dbg, TT_DEBUG_PAGE_ID);
                 page = min(max(page, 0), a.num_pages - 1);
             }
             const long long off = (((long long)page * a.Hkv + g) * a.page_size + j % a.page_size) * D;
@@ -74,23 +95,37 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(F32Args a) {
             kp = a.Kd + off;
             vp = a.Vd + off;
         }
-        float k[E], v[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            k[e] = kp[lane * E + e];
-            v[e] = vp[lane * E + e];
+        // score of key j: its row against the query row, 4 elements at a time
+        float dot = 0.f;
+#pragma unroll 8
+        for (int d = 0; d < D; d += 4) {
+            const f32x4 kv = *reinterpret_cast<const f32x4*>(kp + d);
+            const f32x4 qv = *reinterpret_cast<const f32x4*>(&qs[w][d]);
+            dot = __builtin_fmaf(kv[0], qv[0], dot);
+            dot = __builtin_fmaf(kv[1], qv[1], dot);
+            dot = __builtin_fmaf(kv[2], qv[2], dot);
+            dot = __builtin_fmaf(kv[3], qv[3], dot);
         }
-        float part = 0.f;
-#pragma unroll
-        for (int e = 0; e < E; ++e) part = __builtin_fmaf(q[e], k[e], part);
-        const float sc = wave_sum(part) * a.scale;
-        const float mn = fmaxf(m, sc);
+        const bool valid = j0 + lane < n;
+        const float sc = valid ? dot * a.scale : -INFINITY;
+        const float mn = fmaxf(m, wave_max(sc));
         const float alpha = expf(m - mn);  // 0 when m = -inf
-        const float p = expf(sc - mn);
-        l = l * alpha + p;
+        const float p = valid ? expf(sc - mn) : 0.f;
+        l = l * alpha + wave_sum(p);
 #pragma unroll
-        for (int e = 0; e < E; ++e) o[e] = __builtin_fmaf(p, v[e], o[e] * alpha);
+        for (int e = 0; e < E; ++e) o[e] *= alpha;
         m = mn;
+        // O += sum over the chunk's keys t of p_t * V_t, lanes over head_dim
+        const int nt = min(64, n - j0);
+        const unsigned long long vaddr = reinterpret_cast<unsigned long long>(vp);
+        for (int t = 0; t < nt; ++t) {
+            const float pt = __shfl(p, t);
+            const unsigned long long va = ((unsigned long long)(unsigned)__shfl((int)(vaddr >> 32), t) << 32) |
+                                          (unsigned)__shfl((int)(unsigned)vaddr, t);
+            const float* vt = reinterpret_cast<const float*>(va);
+#pragma unroll
+            for (int e = 0; e < E; ++e) o[e] = __builtin_fmaf(pt, vt[lane * E + e], o[e]);
+        }
     }
     float* op = a.O + b * a.osb + s * a.oss + h * a.osh + lane * E;
     const float inv = n > 0 ? 1.f / l : 0.f;
