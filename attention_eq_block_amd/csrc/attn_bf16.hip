@@ -57,6 +57,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 constexpr int kWaves = 8;       // 32 query rows each; waves 0-3 load K, waves 4-7 load V
 constexpr int kThreads = 64 * kWaves;
 constexpr int kFinThreads = 256;
+constexpr int kFinChunks = kRows / (kFinThreads / 16);  // merge workgroups per pair
 constexpr float kTau = 8.0f;  // lazy rescale threshold (log2 units)
 
 constexpr float kLn2 = 0.693147180559945309f;
@@ -914,13 +915,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
 // Merge the per-segment partials of every pair that segment boundaries cut,
 // and write O = 0, LSE = -inf for pairs with no keys at all. The pair's
 // segments follow from the unit counts the main kernel left in the workspace.
-// Grid: n_pairs * 16 workgroups of 256 threads, 16 rows each; a row's 16
-// threads take D/16 consecutive elements each, and every partial a thread
-// reads is an independent load.
+// Grid: n_pairs * kFinChunks workgroups of 256 threads, 16 rows each; a row's
+// 16 threads take D/16 consecutive elements each. Partials are read eight at
+// a time, every load of a group issued before any is used, and the next group
+// is in flight while one is merged, so that a pair cut into many segments
+// costs few memory round trips.
 template <int D, bool F32>
 __global__ __launch_bounds__(kFinThreads) void attn_bf16_finalize(Args a, const int* __restrict__ ctx_len) {
+    constexpr int RPW = kFinThreads / 16;   // rows per workgroup
+    constexpr int EPT = D / 16;             // elements per thread
+    constexpr int NG = 8;                   // partials per group
     const int mult = a.Hkv * a.n_rb;
-    const int p = blockIdx.x / 16, chunk = blockIdx.x % 16;
+    const int p = blockIdx.x / kFinChunks, chunk = blockIdx.x % kFinChunks;
     const int b = p / mult, pl = p % mult;
     const int g = pl / a.n_rb, rb = pl % a.n_rb;
     const int W = a.units_before[0];
@@ -935,60 +941,66 @@ __global__ __launch_bounds__(kFinThreads) void attn_bf16_finalize(Args a, const 
         if (s0 == s1) return;  // written by the main kernel
     }
     const int tid = threadIdx.x;
-    const int rl = chunk * 16 + tid / 16;      // row within the block
+    const int rl = chunk * RPW + tid / 16;  // row within the block
     const int rr = rb * kRows + rl;
     if (rr >= a.S * a.G) return;
     const int s = rr / a.G, h = g * a.G + rr % a.G;
     const long long ob = (long long)b * a.osb + (long long)s * a.oss + (long long)h * a.osh;
-    // Partials in groups of four, the LSEs and rows of a group loaded together
-    // (an index past s1 rereads slot s1 and gets weight 0) and the next group
-    // loaded while one is merged; the running max M and the sums are rescaled
-    // when a group raises M.
-    constexpr int EPT = D / 16;  // elements per thread
     const int d0 = (tid % 16) * EPT;
     typedef float f32xE __attribute__((ext_vector_type(EPT)));
     typedef __bf16 bf16xE __attribute__((ext_vector_type(EPT)));
-    float M = -INFINITY, Wsum = 0.f;
-    f32xE acc = {};
-    auto load = [&](int sg0, float (&l)[4], f32xE (&v)[4]) __attribute__((always_inline)) {
+    typedef typename std::conditional<F32, f32xE, bf16xE>::type raw_t;
+    struct Group {
+        float l[NG];
+        raw_t v[NG];
+    };
+    // partials past s1 are not read (the bound is uniform over the workgroup)
+    auto load = [&](int sg0, Group& gr) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const long long slot = min(sg0 + j, s1) + p;
-            l[j] = a.part_lse[slot * kRows + rl];
+        for (int j = 0; j < NG; ++j) {
+            if (sg0 + j > s1) break;
+            const long long slot = sg0 + j + p;
+            gr.l[j] = a.part_lse[slot * kRows + rl];
             const long long pe = (slot * kRows + rl) * D + d0;
             if constexpr (F32)
-                v[j] = *reinterpret_cast<const f32xE*>(a.part_o + pe);
+                gr.v[j] = *reinterpret_cast<const f32xE*>(a.part_o + pe);
             else
-                v[j] = __builtin_convertvector(
-                    *reinterpret_cast<const bf16xE*>(reinterpret_cast<const __bf16*>(a.part_o) + pe), f32xE);
+                gr.v[j] = *reinterpret_cast<const bf16xE*>(reinterpret_cast<const __bf16*>(a.part_o) + pe);
         }
     };
-    auto merge = [&](int sg0, const float (&l)[4], const f32xE (&v)[4]) __attribute__((always_inline)) {
+    float M = -INFINITY, Wsum = 0.f;
+    f32xE acc = {};
+    auto merge = [&](int sg0, const Group& gr) __attribute__((always_inline)) {
         float mg = M;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (sg0 + j <= s1) mg = fmaxf(mg, l[j]);
+        for (int j = 0; j < NG; ++j) {
+            if (sg0 + j > s1) break;
+            mg = fmaxf(mg, gr.l[j]);
+        }
         if (mg == -INFINITY) return;
         const float sc = __expf(M - mg);  // 0 while M is -inf
         Wsum *= sc;
         acc *= sc;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float w = (sg0 + j <= s1 && l[j] != -INFINITY) ? __expf(l[j] - mg) : 0.f;
+        for (int j = 0; j < NG; ++j) {
+            if (sg0 + j > s1) break;
+            const float w = gr.l[j] != -INFINITY ? __expf(gr.l[j] - mg) : 0.f;
             Wsum += w;
-            acc += w * v[j];
+            if constexpr (F32)
+                acc += w * gr.v[j];
+            else
+                acc += w * __builtin_convertvector(gr.v[j], f32xE);
         }
         M = mg;
     };
-    float la[4], lb[4];
-    f32xE va[4], vb[4];
-    if (s0 <= s1) load(s0, la, va);
-    for (int sg0 = s0; sg0 <= s1; sg0 += 8) {
-        if (sg0 + 4 <= s1) load(sg0 + 4, lb, vb);
-        merge(sg0, la, va);
-        if (sg0 + 4 > s1) break;
-        if (sg0 + 8 <= s1) load(sg0 + 8, la, va);
-        merge(sg0 + 4, lb, vb);
+    Group ga, gb;
+    if (s0 <= s1) load(s0, ga);
+    for (int sg0 = s0; sg0 <= s1; sg0 += 2 * NG) {
+        if (sg0 + NG <= s1) load(sg0 + NG, gb);
+        merge(sg0, ga);
+        if (sg0 + NG > s1) break;
+        if (sg0 + 2 * NG <= s1) load(sg0 + 2 * NG, ga);
+        merge(sg0 + NG, gb);
     }
     const float inv = Wsum > 0.f ? 1.f / Wsum : 0.f;
     const f32xE o = acc * inv;
@@ -1089,7 +1101,7 @@ tt_status launch_attn_bf16(const tt_block_attn_params& p, const AttnPlan& pl, vo
         while ((1 << a.page_shift) < p.page_size) ++a.page_shift;
     }
     const bool p2 = a.page_shift >= 0;
-    const dim3 grid(pl.n_seg), blk(kThreads), fgrid(pl.n_pairs * 16), fblk(kFinThreads);
+    const dim3 grid(pl.n_seg), blk(kThreads), fgrid(pl.n_pairs * kFinChunks), fblk(kFinThreads);
     if (p.head_dim == 128) {
         if (p2) hipLaunchKernelGGL((attn_bf16_kernel<128, true>), grid, blk, 0, s, a, a.page_table, a.ctx_len);
         else hipLaunchKernelGGL((attn_bf16_kernel<128, false>), grid, blk, 0, s, a, a.page_table, a.ctx_len);
