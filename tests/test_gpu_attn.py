@@ -43,6 +43,48 @@ def test_single_bf16(variant):
     print(run_full(synth.attn_case("single", variant)))
 
 
+def pieces_per_pair(c, n_cu, piece_cost=3, tile=64, rows=256):
+    """Segments that cut each (sequence, kv head, row block) pair of a bf16 call: the
+    work split the library plans (one equal-cost segment per workgroup, a pair costing
+    its tiles plus piece_cost), redone on the host to choose shapes for the test below."""
+    G = c.Hq // c.Hkv
+    n_rb = -(-c.S * G // rows)
+    mult = c.Hkv * n_rb
+    has_den = 1 if c.with_den else 0
+    units = [-(-int(L) // tile) + has_den for L in c.ctx_lens]
+    w_max = c.B * mult * max(units)
+    cu8 = -(-n_cu // 8) * 8
+    nseg = min(max(-(-((w_max + 1) // 2) // 8) * 8, 8), cu8)
+    weighted = [mult * (u + piece_cost) if u > 0 else 0 for u in units]
+    seg_len = -(-sum(weighted) // nseg)
+    out, before = [], 0
+    for u, w in zip(units, weighted):
+        for pl in range(mult):
+            if u > 0:
+                U = before + pl * (u + piece_cost) + piece_cost
+                out.append((U + u - 1) // seg_len - U // seg_len + 1)
+        before += w
+    return out
+
+
+def test_merge_group_boundaries():
+    """Pairs cut into 2, 8, 9, 16, 17 and 24-25 pieces: the merge reads partials eight
+    at a time with the next group in flight, so these are its group edges (one group,
+    a full group, a second group, two full groups, a third)."""
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    found = {}
+    for L in range(64, 8192, 16):
+        c = case(1, 16, 32, 2, 128, [L])
+        for k in pieces_per_pair(c, n_cu):
+            for want in (2, 8, 9, 16, 17, 24, 25):
+                if k == want and want not in found:
+                    found[want] = L
+    assert {8, 9, 16, 17}.issubset(found), found
+    for want, L in sorted(found.items()):
+        c = case(1, 16, 32, 2, 128, [L])
+        print(want, L, run_full(c, what=f"{want} pieces, prefix {L}"))
+
+
 def test_ragged_bf16_full_size():
     """B=64, prefix 16*U{32..512}, shuffled 16-token pages: every row at full size."""
     c = synth.attn_case("ragged")
