@@ -6,7 +6,9 @@ section 2.2) over a batch: the block starts fully masked; each denoising step
 r = 1..T runs the Eq. (1) block attention of all six attention layers (each
 against its own layer-aligned context cache) and then one ConfidenceSample
 (threshold gamma, steps left T-r+1); the loop stops once every position is
-committed. The denoiser layers between attention and the logits need trained
+committed. Every call is launched from the host; --graph replays each step from a HIP graph
+captured once per step instead (after checking that the graphs reproduce the host-launched
+loop exactly). The denoiser layers between attention and the logits need trained
 weights and are not part of this path: each step's logits are synthetic
 (N(0,1) plus a spike of height 0.5*t at a fixed target), drawn in advance and
 resident in HBM, as are the six caches.
@@ -402,48 +404,94 @@ def run_loop(args, stream):
     sh = stream.cuda_stream
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(T)]
 
-    def block(gamma, timing=False):
+    def enqueue_step(r, gamma, handle, timing=False):
+        """Step r of Algorithm 2 on the stream `handle`: six Eq. (1) layers, one ConfidenceSample,
+        and the copy of the masked counts to pinned host memory."""
+        if timing:
+            ev[r - 1][0].record(stream)
+        for L in layers:
+            L(handle)
+        if timing:
+            ev[r - 1][1].record(stream)
+        up.gamma = gamma
+        up.logits = logits[r - 1].data_ptr()
+        up.steps_left = T - r + 1
+        if unis:
+            up.uniforms = unis[r - 1].data_ptr()
+        rc = lib.tt_conf_unmask(up, uws.data_ptr(), uws.numel(), handle)
+        if rc:
+            raise RuntimeError(f"tt_conf_unmask failed: {api.status_string(rc)}")
+        nm_host.copy_(nmask, non_blocking=True)
+
+    # --graph: one HIP graph per step and gamma (the step's kernel arguments are fixed), so that
+    # after the host reads a step's masked count the next step starts with one graph launch rather
+    # than fourteen library calls. The library allocates and clears nothing, so a step captures
+    # whole. On MI355X the replays measured slower than host launches (4.52 against 4.44 ms per
+    # block), so they are not the default.
+    graphs = {}
+
+    def step_graphs(gamma):
+        if gamma not in graphs:
+            torch.cuda.synchronize()
+            cs = torch.cuda.Stream()
+            gs = []
+            for r in range(1, T + 1):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cs):
+                    enqueue_step(r, gamma, cs.cuda_stream)
+                gs.append(g)
+            torch.cuda.synchronize()
+            graphs[gamma] = gs
+        return graphs[gamma]
+
+    def block(gamma, timing=False, graph=False):
         tokens.fill_(synth.MASK_TOKEN_ID)
         mask.fill_(1)
-        up.gamma = gamma
+        gs = step_graphs(gamma) if graph else None
         steps = 0
         for r in range(1, T + 1):
-            if timing:
-                ev[r - 1][0].record(stream)
-            for L in layers:
-                L(sh)
-            if timing:
-                ev[r - 1][1].record(stream)
-            up.logits = logits[r - 1].data_ptr()
-            up.steps_left = T - r + 1
-            if unis:
-                up.uniforms = unis[r - 1].data_ptr()
-            rc = lib.tt_conf_unmask(up, uws.data_ptr(), uws.numel(), sh)
-            if rc:
-                raise RuntimeError(f"tt_conf_unmask failed: {api.status_string(rc)}")
+            if gs:
+                gs[r - 1].replay()
+            else:
+                enqueue_step(r, gamma, sh, timing)
             steps = r
-            nm_host.copy_(nmask, non_blocking=True)
             stream.synchronize()
             if int(nm_host.sum()) == 0:
                 break
         return steps
 
-    def timed_blocks(gamma, k, warmup):
+    def timed_blocks(gamma, k, warmup, graph):
         for _ in range(warmup):
-            block(gamma)
+            block(gamma, graph=graph)
         torch.cuda.synchronize()
-        per_call, total_steps = [], 0
+        total_steps = 0
         t0 = time.perf_counter()
         for _ in range(k):
+            total_steps += block(gamma, graph=graph)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, total_steps
+
+    def timed_calls(gamma, k):
+        """Per-call attention times: HIP events around each step's six calls, eager launches."""
+        per_call = []
+        for _ in range(k):
             n = block(gamma, timing=True)
-            total_steps += n
             torch.cuda.synchronize()
             per_call += [ev[r][0].elapsed_time(ev[r][1]) / NL for r in range(n)]
-        torch.cuda.synchronize()
-        return time.perf_counter() - t0, total_steps, per_call
+        return per_call
 
-    log("[bench] warmup and timed blocks")
-    wall, total_steps, per_call = timed_blocks(args.gamma, args.steps, args.warmup)
+    use_graph = args.graph
+    if use_graph:
+        # the graphs must reproduce the eager block exactly
+        n_e = block(args.gamma)
+        ref = (tokens.clone(), mask.clone(), nmask.clone())
+        n_g = block(args.gamma, graph=True)
+        torch.cuda.synchronize()
+        if n_g != n_e or not all(torch.equal(x, y) for x, y in zip(ref, (tokens, mask, nmask))):
+            raise RuntimeError("graph replay of the denoise loop differs from the eager loop")
+    log("[bench] warmup and timed blocks" + (" (one graph launch per step)" if use_graph else ""))
+    wall, total_steps = timed_blocks(args.gamma, args.steps, args.warmup, use_graph)
+    per_call = timed_calls(args.gamma, max(3, args.steps // 2))
     ms_per_block = wall * 1e3 / args.steps
     steps_per_block = total_steps / args.steps
     value = B * S * NL * total_steps / wall
@@ -460,7 +508,7 @@ def run_loop(args, stream):
                                  "tokens_per_s": value}
                 continue
             k = max(3, args.steps // 2)
-            w, ts, _ = timed_blocks(g, k, 1)
+            w, ts = timed_blocks(g, k, 1, use_graph)
             sweep[str(g)] = {"blocks_per_s": B * k / w, "steps_per_block": ts / k,
                              "tokens_per_s": B * S * NL * ts / w}
     wl = ("full-block denoise loop (Algorithm 2): batch 32, S=16, T=16, 6 attention layers, prefix 8192, "
@@ -473,7 +521,11 @@ def run_loop(args, stream):
         "config": {"workload": wl, "global_batch": B, "seq_len": case.ctx_lens[0] + S, "parallelism": "none",
                    "denoise_steps_per_block": steps_per_block, "blocks_per_s": B * args.steps / wall,
                    "attn_call_us": call_ms * 1e3, "attn_call_tokens_per_s": B * S / (call_ms * 1e-3),
-                   "attn_call_us_spread": spread_us(per_call)},
+                   "attn_call_us_spread": spread_us(per_call),
+                   "launch": "one HIP graph per denoising step (checked against the eager loop)" if use_graph
+                   else "each call launched from the host",
+                   "attn_call_timing": "HIP events around each step's six calls, eager launches, in blocks run "
+                                       "right after the timed ones"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": "tt_block_attn (attn_bf16_kernel + attn_bf16_finalize), one layer",
@@ -696,6 +748,9 @@ def main():
     ap.add_argument("--no-configs", action="store_true",
                     help="loop workload only: skip the per-config lines of the other four workloads")
     ap.add_argument("--copy-calibration", action="store_true", help="run only the counter-reference copy")
+    ap.add_argument("--graph", action="store_true",
+                    help="loop workload: replay each denoising step from a HIP graph instead of launching its calls "
+                         "from the host (measured slower on MI355X)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path (the data-parallel "
