@@ -411,10 +411,20 @@ __device__ __forceinline__ void dma_tile(uint8_t* lbuf, const Cur& c, int page, 
         }
     }
     uint8_t* const dst = lbuf + 16 * wq * C::ROWB;
+    // With one row block per (sequence, kv head) every K/V byte is read once: the loads
+    // are non-temporal (nt), so the stream does not displace cached data. With more
+    // row blocks the other blocks read the same tiles, and the caches may still hold them.
+    if (a.n_rb == 1) {
 #pragma unroll
-    for (int k = 0; k < C::LPG; ++k)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + 1024 * k), 16,
-                                                 off[k], 0, 0, 0);
+        for (int k = 0; k < C::LPG; ++k)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + 1024 * k),
+                                                     16, off[k], 0, 0, 2);
+    } else {
+#pragma unroll
+        for (int k = 0; k < C::LPG; ++k)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + 1024 * k),
+                                                     16, off[k], 0, 0, 0);
+    }
 }
 
 template <int D, bool P2>
