@@ -925,16 +925,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
 // Merge the per-segment partials of every pair that segment boundaries cut,
 // and write O = 0, LSE = -inf for pairs with no keys at all. The pair's
 // segments follow from the unit counts the main kernel left in the workspace.
-// Grid: n_pairs * kFinChunks workgroups of 256 threads, 16 rows each; a row's
-// 16 threads take D/16 consecutive elements each. Partials are read eight at
-// a time, every load of a group issued before any is used, and the next group
-// is in flight while one is merged, so that a pair cut into many segments
-// costs few memory round trips.
-template <int D, bool F32>
-__global__ __launch_bounds__(kFinThreads) void attn_bf16_finalize(Args a, const int* __restrict__ ctx_len) {
+// Grid: n_pairs * kFinChunks workgroups of PS * 256 threads, 16 rows each; a
+// row's 16 threads take D/16 consecutive elements each. Partials are read eight
+// at a time, every load of a group issued before any is used, and the next group
+// is in flight while one is merged. With PS > 1 (pairs cut into many pieces)
+// thread group q of the workgroup takes every PS-th partial from the q-th, and
+// group 0 merges the groups' results from LDS in group order; so a pair cut into
+// many segments costs few memory round trips.
+template <int D, bool F32, int PS>
+__global__ __launch_bounds__(kFinThreads * PS) void attn_bf16_finalize(Args a, const int* __restrict__ ctx_len) {
     constexpr int RPW = kFinThreads / 16;   // rows per workgroup
     constexpr int EPT = D / 16;             // elements per thread
-    constexpr int NG = 8;                   // partials per group
+    constexpr int NG = F32 && PS > 1 ? 4 : 8;  // partials per group (fp32 ones in four at most 128 registers)
     const int mult = a.Hkv * a.n_rb;
     const int p = blockIdx.x / kFinChunks, chunk = blockIdx.x % kFinChunks;
     const int b = p / mult, pl = p % mult;
@@ -950,10 +952,12 @@ __global__ __launch_bounds__(kFinThreads) void attn_bf16_finalize(Args a, const 
         s1 = (U + units - 1) / seg_len;
         if (s0 == s1) return;  // written by the main kernel
     }
-    const int tid = threadIdx.x;
+    const int grp = threadIdx.x / kFinThreads;  // partial group (PS > 1)
+    const int tid = threadIdx.x % kFinThreads;
     const int rl = chunk * RPW + tid / 16;  // row within the block
     const int rr = rb * kRows + rl;
-    if (rr >= a.S * a.G) return;
+    const bool live = rr < a.S * a.G;
+    if (PS == 1 && !live) return;
     const int s = rr / a.G, h = g * a.G + rr % a.G;
     const long long ob = (long long)b * a.osb + (long long)s * a.oss + (long long)h * a.osh;
     const int d0 = (tid % 16) * EPT;
@@ -964,12 +968,12 @@ __global__ __launch_bounds__(kFinThreads) void attn_bf16_finalize(Args a, const 
         float l[NG];
         raw_t v[NG];
     };
-    // partials past s1 are not read (the bound is uniform over the workgroup)
+    // partials past s1 are not read (the bound is uniform over the thread group)
     auto load = [&](int sg0, Group& gr) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < NG; ++j) {
-            if (sg0 + j > s1) break;
-            const long long slot = sg0 + j + p;
+            if (sg0 + PS * j > s1) break;
+            const long long slot = sg0 + PS * j + p;
             gr.l[j] = a.part_lse[slot * kRows + rl];
             const long long pe = (slot * kRows + rl) * D + d0;
             if constexpr (F32)
@@ -984,7 +988,7 @@ __global__ __launch_bounds__(kFinThreads) void attn_bf16_finalize(Args a, const 
         float mg = M;
 #pragma unroll
         for (int j = 0; j < NG; ++j) {
-            if (sg0 + j > s1) break;
+            if (sg0 + PS * j > s1) break;
             mg = fmaxf(mg, gr.l[j]);
         }
         if (mg == -INFINITY) return;
@@ -993,7 +997,7 @@ __global__ __launch_bounds__(kFinThreads) void attn_bf16_finalize(Args a, const 
         acc *= sc;
 #pragma unroll
         for (int j = 0; j < NG; ++j) {
-            if (sg0 + j > s1) break;
+            if (sg0 + PS * j > s1) break;
             const float w = gr.l[j] != -INFINITY ? __expf(gr.l[j] - mg) : 0.f;
             Wsum += w;
             if constexpr (F32)
@@ -1004,13 +1008,39 @@ __global__ __launch_bounds__(kFinThreads) void attn_bf16_finalize(Args a, const 
         M = mg;
     };
     Group ga, gb;
-    if (s0 <= s1) load(s0, ga);
-    for (int sg0 = s0; sg0 <= s1; sg0 += 2 * NG) {
-        if (sg0 + NG <= s1) load(sg0 + NG, gb);
-        merge(sg0, ga);
-        if (sg0 + NG > s1) break;
-        if (sg0 + 2 * NG <= s1) load(sg0 + 2 * NG, ga);
-        merge(sg0 + NG, gb);
+    const int q0 = s0 + grp;  // this group's first partial
+    constexpr int STEP = PS * NG;
+    if (live && q0 <= s1) {
+        load(q0, ga);
+        for (int sg0 = q0; sg0 <= s1; sg0 += 2 * STEP) {
+            if (sg0 + STEP <= s1) load(sg0 + STEP, gb);
+            merge(sg0, ga);
+            if (sg0 + STEP > s1) break;
+            if (sg0 + 2 * STEP <= s1) load(sg0 + 2 * STEP, ga);
+            merge(sg0 + STEP, gb);
+        }
+    }
+    if constexpr (PS > 1) {
+        // groups 1..PS-1 hand (M, Wsum, acc) to group 0, which merges them in group order
+        __shared__ float xm[PS - 1][kFinThreads], xw[PS - 1][kFinThreads];
+        __shared__ f32xE xa[PS - 1][kFinThreads];
+        if (grp > 0) {
+            xm[grp - 1][tid] = M;
+            xw[grp - 1][tid] = Wsum;
+            xa[grp - 1][tid] = acc;
+        }
+        __syncthreads();
+        if (grp > 0 || !live) return;
+#pragma unroll
+        for (int q = 0; q < PS - 1; ++q) {
+            const float mq = xm[q][tid];
+            const float mg = fmaxf(M, mq);
+            if (mg == -INFINITY) continue;
+            const float sa = __expf(M - mg), sb = __expf(mq - mg);  // 0 for a side still at -inf
+            Wsum = Wsum * sa + xw[q][tid] * sb;
+            acc = acc * sa + xa[q][tid] * sb;
+            M = mg;
+        }
     }
     const float inv = Wsum > 0.f ? 1.f / Wsum : 0.f;
     const f32xE o = acc * inv;
@@ -1073,6 +1103,9 @@ AttnPlan plan_attn_bf16(const tt_block_attn_params& p, int n_cu) {
     pl.ws_part_lse = (size_t)pl.n_slots * kRows * sizeof(float);
     pl.ws_units = ((size_t)(p.B + 1) * sizeof(int) + 255) / 256 * 256;
     pl.ws_total = pl.ws_part_o + pl.ws_part_lse + pl.ws_units + 256;
+    // pairs cut into many pieces on average (16 or more): the merge splits each
+    // pair's partials over four thread groups
+    pl.fin_split = (long long)pl.n_seg >= 16LL * pl.n_pairs ? 4 : 1;
     return pl;
 }
 
@@ -1111,17 +1144,28 @@ tt_status launch_attn_bf16(const tt_block_attn_params& p, const AttnPlan& pl, vo
         while ((1 << a.page_shift) < p.page_size) ++a.page_shift;
     }
     const bool p2 = a.page_shift >= 0;
-    const dim3 grid(pl.n_seg), blk(kThreads), fgrid(pl.n_pairs * kFinChunks), fblk(kFinThreads);
+    const dim3 grid(pl.n_seg), blk(kThreads), fgrid(pl.n_pairs * kFinChunks), fblk(kFinThreads),
+        fblk4(4 * kFinThreads);
     if (p.head_dim == 128) {
         if (p2) hipLaunchKernelGGL((attn_bf16_kernel<128, true>), grid, blk, 0, s, a, a.page_table, a.ctx_len);
         else hipLaunchKernelGGL((attn_bf16_kernel<128, false>), grid, blk, 0, s, a, a.page_table, a.ctx_len);
-        if (a.o_f32) hipLaunchKernelGGL((attn_bf16_finalize<128, true>), fgrid, fblk, 0, s, a, a.ctx_len);
-        else hipLaunchKernelGGL((attn_bf16_finalize<128, false>), fgrid, fblk, 0, s, a, a.ctx_len);
+        if (pl.fin_split > 1) {
+            if (a.o_f32) hipLaunchKernelGGL((attn_bf16_finalize<128, true, 4>), fgrid, fblk4, 0, s, a, a.ctx_len);
+            else hipLaunchKernelGGL((attn_bf16_finalize<128, false, 4>), fgrid, fblk4, 0, s, a, a.ctx_len);
+        } else {
+            if (a.o_f32) hipLaunchKernelGGL((attn_bf16_finalize<128, true, 1>), fgrid, fblk, 0, s, a, a.ctx_len);
+            else hipLaunchKernelGGL((attn_bf16_finalize<128, false, 1>), fgrid, fblk, 0, s, a, a.ctx_len);
+        }
     } else {
         if (p2) hipLaunchKernelGGL((attn_bf16_kernel<64, true>), grid, blk, 0, s, a, a.page_table, a.ctx_len);
         else hipLaunchKernelGGL((attn_bf16_kernel<64, false>), grid, blk, 0, s, a, a.page_table, a.ctx_len);
-        if (a.o_f32) hipLaunchKernelGGL((attn_bf16_finalize<64, true>), fgrid, fblk, 0, s, a, a.ctx_len);
-        else hipLaunchKernelGGL((attn_bf16_finalize<64, false>), fgrid, fblk, 0, s, a, a.ctx_len);
+        if (pl.fin_split > 1) {
+            if (a.o_f32) hipLaunchKernelGGL((attn_bf16_finalize<64, true, 4>), fgrid, fblk4, 0, s, a, a.ctx_len);
+            else hipLaunchKernelGGL((attn_bf16_finalize<64, false, 4>), fgrid, fblk4, 0, s, a, a.ctx_len);
+        } else {
+            if (a.o_f32) hipLaunchKernelGGL((attn_bf16_finalize<64, true, 1>), fgrid, fblk, 0, s, a, a.ctx_len);
+            else hipLaunchKernelGGL((attn_bf16_finalize<64, false, 1>), fgrid, fblk, 0, s, a, a.ctx_len);
+        }
     }
     return hipGetLastError() == hipSuccess ? TT_OK : TT_ERR_HIP;
 }

@@ -83,6 +83,12 @@ def test_merge_group_boundaries():
     for want, L in sorted(found.items()):
         c = case(1, 16, 32, 2, 128, [L])
         print(want, L, run_full(c, what=f"{want} pieces, prefix {L}"))
+    # float32 output (fp32 partials) where the merge splits each pair over four thread groups
+    c = synth.attn_case("single")
+    inp = synth.make_attn_inputs(c, seed=2)
+    O, Ls = gpu_attn(inp, o_dtype=torch.float32)
+    Or, Lr = oracle_attn(inp)
+    print("single, fp32 output", check_attn(O, Ls, Or, Lr, c.dtype, "single fp32 out"))
 
 
 def test_ragged_bf16_full_size():
