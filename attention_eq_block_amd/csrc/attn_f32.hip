@@ -1,11 +1,11 @@
 // Eq. (1) of Nemotron-TwoTower (arXiv 2606.26493, section 2.1) for float32
 // inputs: one wavefront per query row (b, s, h). Keys are taken 64 at a time,
 // one per lane: each lane computes its key's score against the query row
-// (read from LDS as a broadcast), one wave reduction per 64 keys gives the
-// running max and sum (online softmax in float32), and the P.V product runs
-// with lanes over head_dim, each key's weight broadcast from its lane. This
-// path serves float32 callers and small shapes; the bf16 MFMA path is the
-// throughput path.
+// (read from LDS as a broadcast) and copies its key's value row into the
+// wave's LDS tile, one wave reduction per 64 keys gives the running max and
+// sum (online softmax in float32), and the P.V product runs with lanes over
+// head_dim, reading the weights and value rows from LDS. This path serves
+// float32 callers and small shapes; the bf16 MFMA path is the throughput path.
 #include "tt_internal.h"
 
 namespace tt {
@@ -47,6 +47,9 @@ template <int D>
 __global__ __launch_bounds__(256) void attn_f32_kernel(F32Args a) {
     constexpr int E = D / 64;  // elements of head_dim per lane in the P.V product
     __shared__ __attribute__((aligned(16))) float qs[4][D];
+    // each wave's 64 value rows (padded pitch: the row-per-lane writes spread over the banks) and weights
+    __shared__ __attribute__((aligned(16))) float vs[4][64][D + 4];
+    __shared__ float ps[4][64];
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     const long long row = (long long)blockIdx.x * 4 + w;
@@ -95,6 +98,10 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(F32Args a) {
             kp = a.Kd + off;
             vp = a.Vd + off;
         }
+        // this lane's value row into the wave's LDS tile (its loads go out with the key row's)
+#pragma unroll
+        for (int d = 0; d < D; d += 4)
+            *reinterpret_cast<f32x4*>(&vs[w][lane][d]) = *reinterpret_cast<const f32x4*>(vp + d);
         // score of key j: its row against the query row, 4 elements at a time
         float dot = 0.f;
 #pragma unroll 8
@@ -115,17 +122,22 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(F32Args a) {
 #pragma unroll
         for (int e = 0; e < E; ++e) o[e] *= alpha;
         m = mn;
-        // O += sum over the chunk's keys t of p_t * V_t, lanes over head_dim
+        // O += sum over the chunk's keys t of p_t * V_t, lanes over head_dim, from LDS
+        ps[w][lane] = p;
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         const int nt = min(64, n - j0);
-        const unsigned long long vaddr = reinterpret_cast<unsigned long long>(vp);
+#pragma unroll 8
         for (int t = 0; t < nt; ++t) {
-            const float pt = __shfl(p, t);
-            const unsigned long long va = ((unsigned long long)(unsigned)__shfl((int)(vaddr >> 32), t) << 32) |
-                                          (unsigned)__shfl((int)(unsigned)vaddr, t);
-            const float* vt = reinterpret_cast<const float*>(va);
+            const float pt = ps[w][t];
 #pragma unroll
-            for (int e = 0; e < E; ++e) o[e] = __builtin_fmaf(pt, vt[lane * E + e], o[e]);
+            for (int e = 0; e < E; ++e) o[e] = __builtin_fmaf(pt, vs[w][t][lane * E + e], o[e]);
         }
+        // the next chunk rewrites the tile only after these reads
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
     float* op = a.O + b * a.osb + s * a.oss + h * a.osh + lane * E;
     const float inv = n > 0 ? 1.f / l : 0.f;
