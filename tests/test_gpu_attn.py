@@ -222,6 +222,18 @@ def test_head_dim_64(dtype):
     print(run_full(c))
 
 
+@pytest.mark.parametrize("o_dtype", [None, torch.float32])
+def test_head_dim_64_many_pieces(o_dtype):
+    """One sequence with a 4096-token prefix at head_dim 64: every pair is cut into about 33
+    pieces, so the merge splits each pair's partials over four thread groups (bf16 and fp32
+    partials)."""
+    c = case(1, 16, 32, 2, 64, [4096])
+    inp = synth.make_attn_inputs(c, seed=4)
+    O, L = gpu_attn(inp, o_dtype=o_dtype)
+    Or, Lr = oracle_attn(inp)
+    print(check_attn(O, L, Or, Lr, c.dtype, f"d=64, 33 pieces, out {o_dtype}"))
+
+
 @pytest.mark.parametrize("page_size", [32, 48, 64, 256])
 def test_page_sizes(page_size):
     c = case(3, 16, 32, 2, 128, [100, 700, 257], page_size=page_size, shuffle_pages=True)
