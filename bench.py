@@ -723,13 +723,32 @@ def run_sample(args):
 
 def copy_calibration():
     """A plain device-to-device copy of COPY_BYTES, five times: the counter reference
-    for FETCH_SIZE / WRITE_SIZE (each launch reads and writes COPY_BYTES)."""
+    for FETCH_SIZE / WRITE_SIZE (each launch reads and writes COPY_BYTES). Also reports
+    the copy's bandwidth and that of a plain read-only reduction over the same buffer
+    (PyTorch kernels), as references for what streaming HBM reaches on the box."""
     src = torch.empty(COPY_BYTES // 4, dtype=torch.int32, device="cuda").fill_(1)
     dst = torch.empty_like(src)
+    fsrc = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+    copy_ms, read_ms = [], []
     for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
         dst.copy_(src)
-    torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 5}))
+        e1.record()
+        torch.cuda.synchronize()
+        copy_ms.append(e0.elapsed_time(e1))
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.sum(fsrc, dim=0, out=sink)
+        e1.record()
+        torch.cuda.synchronize()
+        read_ms.append(e0.elapsed_time(e1))
+    cm, rm = pct(copy_ms, 50), pct(read_ms, 50)
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 5,
+                      "copy_GBps": 2 * COPY_BYTES / (cm * 1e-3) / 1e9, "read_GBps": COPY_BYTES / (rm * 1e-3) / 1e9,
+                      "note": "median of 5; copy counts bytes read plus written"}))
 
 
 def main():
