@@ -123,15 +123,19 @@ def gpu_unmask(logits, mask, tokens, *, gamma, temperature, steps_left, separate
 
 
 def fragile(ref_conf, mask, gamma, steps_left, eps=1e-6):
-    """Per sequence: True when a decision sits within eps of its threshold in the oracle's values."""
+    """Per sequence: True when a decision sits within eps of its threshold in the oracle's values.
+    A step with steps_left = 1 commits every masked position, and with gamma >= 1 no confidence
+    (at most 1) is above gamma: neither decides anything against gamma."""
     B, S = mask.shape
     out = np.zeros(B, dtype=bool)
+    if steps_left == 1:
+        return out
     for b in range(B):
         m = mask[b].astype(bool)
         c = ref_conf[b][m]
         if c.size == 0:
             continue
-        if np.any(np.abs(c - gamma) < eps):
+        if gamma < 1.0 and np.any(np.abs(c - gamma) < eps):
             out[b] = True
             continue
         M = c.size
