@@ -265,7 +265,6 @@ __device__ __forceinline__ int walk_elems(const char* rp, int lo, int hi, float 
 template <bool BF16>
 __global__ __launch_bounds__(256) void sample_locate(UArgs a) {
     const int row = blockIdx.x;
-    if (!a.mask_in[row]) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const long long rows = (long long)a.B * a.S;
     const float c = a.c;
@@ -274,8 +273,16 @@ __global__ __launch_bounds__(256) void sample_locate(UArgs a) {
     __shared__ int wlast[4];
     __shared__ Triple tri[64];                   // n_vsplit <= 64
     __shared__ float tot[kSampleMaxIter + 2];    // head, iterations, tail
-    if (tid < a.n_vsplit) tri[tid] = a.part[(long long)tid * rows + row];
-    if (tid == 128) sh_u = a.uniforms[row];
+    // the mask, the split triples and the uniform in one round trip (an unmasked
+    // row's triples are stale and never used)
+    const uint8_t mk = a.mask_in[row];
+    Triple tr{};
+    if (tid < a.n_vsplit) tr = a.part[(long long)tid * rows + row];
+    float uu = 0.f;
+    if (tid == 128) uu = a.uniforms[row];
+    if (!mk) return;
+    if (tid < a.n_vsplit) tri[tid] = tr;
+    if (tid == 128) sh_u = uu;
     __syncthreads();
     if (tid == 0) {
         float m = -INFINITY, z = 0.f;
@@ -454,19 +461,29 @@ __global__ __launch_bounds__(64) void unmask_select(UArgs a) {
     const int b = blockIdx.x;
     const int l = threadIdx.x;
     const bool inb = l < a.S;
-    const long long row = (long long)b * a.S + l;
-    const bool masked = inb && a.mask_in[row] != 0;
+    const long long row = (long long)b * a.S + (inb ? l : 0);
+    // The mask, the split triples and the draw are all requested before any of
+    // them is used (one memory round trip, not one per dependent read). They are
+    // read for every position of the sequence; an unmasked row's slots hold
+    // stale values, which are never used.
+    const uint8_t mk = a.mask_in[row];
+    Drawn d{INT_MAX, 0.f};
+    if (a.drawn) d = a.drawn[row];
     float m = -INFINITY, z = 0.f;
     int am = INT_MAX;
-    if (masked) {
-        for (int k = 0; k < a.n_vsplit; ++k) {
-            const Triple t = a.part[(long long)k * a.B * a.S + row];
-            combine(m, am, z, t.m, t.a, t.z, a.c);
-        }
+    const long long rows = (long long)a.B * a.S;
+    for (int k0 = 0; k0 < a.n_vsplit; k0 += 8) {
+        Triple t[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (k0 + j < a.n_vsplit) t[j] = a.part[(long long)(k0 + j) * rows + row];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (k0 + j < a.n_vsplit) combine(m, am, z, t[j].m, t[j].a, t[j].z, a.c);
     }
+    const bool masked = inb && mk != 0;
     float conf = masked ? 1.f / z : -INFINITY;
     if (masked && a.drawn) {
-        const Drawn d = a.drawn[row];
         am = d.a;
         conf = d.conf;
     }
@@ -479,11 +496,14 @@ __global__ __launch_bounds__(64) void unmask_select(UArgs a) {
     if (npass >= kmin) {
         commit = pass;
     } else {
+        // rank among the masked positions: their confidences are read lane by
+        // lane (a uniform index: a register read, not an LDS round trip each)
         int rank = 0;
-        for (int j = 0; j < 64; ++j) {
-            const float cj = __shfl(conf, j);
-            const bool mj = (mmask >> j) & 1ull;
-            if (mj && (cj > conf || (cj == conf && j < l))) ++rank;
+        const int cbits = __float_as_int(conf);
+        for (int j = 0; j < a.S; ++j) {
+            if (!((mmask >> j) & 1ull)) continue;
+            const float cj = __int_as_float(__builtin_amdgcn_readlane(cbits, j));
+            rank += (cj > conf || (cj == conf && j < l)) ? 1 : 0;
         }
         commit = masked && rank < kmin;
     }
@@ -562,6 +582,9 @@ UnmaskPlan plan_unmask(const tt_conf_unmask_params& p, int n_cu) {
     const int cu = n_cu > 0 ? n_cu : 256;
     // enough workgroups to cover the chip about 8 times, at least 2048 logits each
     long long want = rows > 0 ? (8LL * cu + rows - 1) / rows : 1;
+    // a stochastic draw re-reads one split of each row: at most 16384 logits per
+    // split (smaller splits measured slower: more reduction workgroups)
+    if (p.uniforms && want < (p.V + 16383) / 16384) want = (p.V + 16383) / 16384;
     long long cap = (p.V + 2047) / 2048;
     if (want > cap) want = cap;
     if (want < 1) want = 1;
