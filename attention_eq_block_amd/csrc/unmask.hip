@@ -197,16 +197,30 @@ __global__ __launch_bounds__(256) void vocab_reduce(UArgs a) {
     }
 }
 
-// The 8 logits of 16-byte-aligned chunk ch of a row body, widened to float.
+// The raw bytes of 16-byte-aligned chunk ch of a row body (8 logits: r0, and
+// r1 too for float32 logits), and the same widened to float.
 template <bool BF16>
-__device__ __forceinline__ void load_chunk(const char* body, int ch, float (&f)[8]) {
+__device__ __forceinline__ void load_raw(const char* body, int ch, u32x4& r0, u32x4& r1) {
     if (BF16) {
-        unpack(*reinterpret_cast<const u32x4*>(body + (long long)ch * 16), f);
+        r0 = *reinterpret_cast<const u32x4*>(body + (long long)ch * 16);
     } else {
-        const u32x4 r0 = *reinterpret_cast<const u32x4*>(body + (long long)ch * 32);
-        const u32x4 r1 = *reinterpret_cast<const u32x4*>(body + (long long)ch * 32 + 16);
+        r0 = *reinterpret_cast<const u32x4*>(body + (long long)ch * 32);
+        r1 = *reinterpret_cast<const u32x4*>(body + (long long)ch * 32 + 16);
+    }
+}
+template <bool BF16>
+__device__ __forceinline__ void widen(const u32x4& r0, const u32x4& r1, float (&f)[8]) {
+    if (BF16) {
+        unpack(r0, f);
+    } else {
         for (int e = 0; e < 4; ++e) { f[e] = __uint_as_float(r0[e]); f[4 + e] = __uint_as_float(r1[e]); }
     }
+}
+template <bool BF16>
+__device__ __forceinline__ void load_chunk(const char* body, int ch, float (&f)[8]) {
+    u32x4 r0, r1;
+    load_raw<BF16>(body, ch, r0, r1);
+    widen<BF16>(r0, r1, f);
 }
 
 // Inclusive sum over the 64 lanes of a wave, in a fixed tree order (the same
@@ -220,19 +234,20 @@ __device__ __forceinline__ float wave_incl_scan(float x, int lane) {
     return x;
 }
 
-// Weights e_v = 2^(x_v c - m c) of one 8-element chunk summed in index order;
-// lastpos becomes the chunk's last index of nonzero weight.
-template <bool BF16>
-__device__ __forceinline__ float chunk_sum(const char* body, int ch, int v0, float c, float mc, float (&e)[8],
-                                           int& lastpos) {
-    float f[8];
-    load_chunk<BF16>(body, ch, f);
+// Weights e_v = 2^(x_v c - m c) of one 8-element chunk (logits f, first index
+// v0) summed in index order; lastpos becomes the chunk's last index of nonzero
+// weight and elast its weight.
+__device__ __forceinline__ float chunk_sum(const float (&f)[8], int v0, float c, float mc, float (&e)[8],
+                                           int& lastpos, float& elast) {
     float cs = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(f[j], c, -mc));
         cs += e[j];
-        if (e[j] > 0.f) lastpos = max(lastpos, v0 + j);
+        if (e[j] > 0.f) {
+            lastpos = max(lastpos, v0 + j);
+            elast = e[j];
+        }
     }
     return cs;
 }
@@ -258,10 +273,12 @@ __device__ __forceinline__ int walk_elems(const char* rp, int lo, int hi, float 
 // holds the crossing is cut into its head (elements before the first aligned
 // chunk, split 0 only), iterations of 64 consecutive chunks (wave i takes
 // iterations i, i + 4, ..., one chunk per lane, so every load is coalesced)
-// and its tail (last split only). The region totals go to LDS; one thread adds
-// them in order and finds the region where the running sum passes the target;
-// that region alone is read again, and inside an iteration the first lane whose
-// scan value passes walks its chunk element by element.
+// and its tail (last split only). The region totals go to LDS; one wave scans
+// them in order and finds the region where the running sum passes the target.
+// Inside an iteration, the first lane whose scan value passes walks its chunk
+// element by element. When the split takes one round of loads (at most 4 NQ
+// iterations), each wave keeps its chunks in registers, so the iteration is
+// not read again.
 template <bool BF16>
 __global__ __launch_bounds__(256) void sample_locate(UArgs a) {
     const int row = blockIdx.x;
@@ -276,12 +293,12 @@ __global__ __launch_bounds__(256) void sample_locate(UArgs a) {
     // the mask, the split triples and the uniform in one round trip (an unmasked
     // row's triples are stale and never used)
     const uint8_t mk = a.mask_in[row];
-    Triple tr{};
-    if (tid < a.n_vsplit) tr = a.part[(long long)tid * rows + row];
+    u32x4 tr = {0u, 0u, 0u, 0u};  // a Triple, as a register vector
+    if (tid < a.n_vsplit) tr = *reinterpret_cast<const u32x4*>(a.part + (long long)tid * rows + row);
     float uu = 0.f;
     if (tid == 128) uu = a.uniforms[row];
     if (!mk) return;
-    if (tid < a.n_vsplit) tri[tid] = tr;
+    if (tid < a.n_vsplit) *reinterpret_cast<u32x4*>(&tri[tid]) = tr;
     if (tid == 128) sh_u = uu;
     __syncthreads();
     if (tid == 0) {
@@ -338,10 +355,11 @@ __global__ __launch_bounds__(256) void sample_locate(UArgs a) {
     // the split's end load its last chunk again and count nothing, so every load
     // is unconditional and they issue together)
     constexpr int NQ = BF16 ? 16 : 8;
+    u32x4 keep0[NQ], keep1[NQ];  // this wave's chunks of the last round of loads
     for (int G0 = w; G0 < NI; G0 += 4 * NQ) {
-        float f[NQ][8];
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) load_chunk<BF16>(body, min(c0 + 64 * (G0 + 4 * q) + lane, c1 - 1), f[q]);
+        for (int q = 0; q < NQ; ++q)
+            load_raw<BF16>(body, min(c0 + 64 * (G0 + 4 * q) + lane, c1 - 1), keep0[q], keep1[q]);
         float cs[NQ], incl[NQ];
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
@@ -349,9 +367,11 @@ __global__ __launch_bounds__(256) void sample_locate(UArgs a) {
             const int ch = c0 + 64 * G + lane;
             cs[q] = 0.f;
             if (G < NI && ch < c1) {
+                float f[8];
+                widen<BF16>(keep0[q], keep1[q], f);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(f[q][j], c, -mc));
+                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(f[j], c, -mc));
                     cs[q] += e;
                     if (e > 0.f) lastpos = max(lastpos, a0 + ch * 8 + j);
                 }
@@ -426,7 +446,26 @@ __global__ __launch_bounds__(256) void sample_locate(UArgs a) {
     const int ch = c0 + 64 * G + lane;
     float e[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     int lpos = -1;
-    const float cs = ch < c1 ? chunk_sum<BF16>(body, ch, a0 + ch * 8, c, mc, e, lpos) : 0.f;
+    float elast = 0.f;  // the weight of lpos
+    float cs = 0.f;
+    if (ch < c1) {
+        float f[8];
+        if (NI <= 4 * NQ) {
+            // iteration G = w + 4 q of the only round: its chunk is still in registers
+            const int q = G >> 2;
+            u32x4 r0 = keep0[0], r1 = keep1[0];
+#pragma unroll
+            for (int qq = 1; qq < NQ; ++qq)
+                if (qq == q) {
+                    r0 = keep0[qq];
+                    r1 = keep1[qq];
+                }
+            widen<BF16>(r0, r1, f);
+        } else {
+            load_chunk<BF16>(body, ch, f);
+        }
+        cs = chunk_sum(f, a0 + ch * 8, c, mc, e, lpos, elast);
+    }
     // the same sums as in pass 1, so lane 63 at least passes
     const float incl = wave_incl_scan(cs, lane);
     float excl = __shfl_up(incl, 1);
@@ -442,7 +481,7 @@ __global__ __launch_bounds__(256) void sample_locate(UArgs a) {
             x += e[j];
             if (v < 0 && x > r && e[j] > 0.f) { v = a0 + ch * 8 + j; ev = e[j]; }
         }
-        if (v < 0 && lpos >= 0) { v = lpos; ev = e[lpos - (a0 + ch * 8)]; }
+        if (v < 0 && lpos >= 0) { v = lpos; ev = elast; }
     }
     if (__shfl(v, first) >= 0) {
         if (lane == first) put(v, ev);
@@ -451,7 +490,7 @@ __global__ __launch_bounds__(256) void sample_locate(UArgs a) {
     // the passing lane's chunk has no weight (a scan rounding): the last weighted lane before it
     const unsigned long long below = __ballot(cs > 0.f && lane < first);
     if (below) {
-        if (lane == 63 - __builtin_clzll(below)) put(lpos, e[lpos - (a0 + ch * 8)]);
+        if (lane == 63 - __builtin_clzll(below)) put(lpos, elast);
     } else if (lane == 0) {
         put(last_all, last_all >= 0 ? weight(last_all) : 0.f);
     }
