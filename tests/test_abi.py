@@ -237,19 +237,19 @@ def test_unmask_sampling_workspace_holds_the_draws():
 
 
 def test_unmask_sampling_vocabulary_bound():
-    """With uniforms a vocabulary split may hold at most 2^21 logits. 4096 rows use one split, so
-    V = 2^21 + 512 is refused with TT_ERR_SHAPE by the host-side validation. The logits and
-    workspace pointers are NULL: were the bound ever to pass, the call would stop at TT_ERR_NULL
-    and still launch nothing."""
+    """With uniforms a vocabulary split may hold at most 2^21 logits, and a drawing step takes at
+    most 64 splits (at least one per 16384 logits), so V = 2^27 + 512 is refused with TT_ERR_SHAPE
+    by the host-side validation and V = 2^27 is not. The logits and workspace pointers are NULL:
+    were the bound ever to pass, the call would stop at TT_ERR_NULL and still launch nothing."""
     L = _lib.lib()
-    big = (1 << 21) + 512
+    big = (1 << 27) + 512
     p = unmask_ok(B=256, S=16, V=big, logits_stride_row=big, uniforms=FAKE, logits=None)
     assert L.tt_conf_unmask_workspace_bytes(ctypes.byref(p)) == 0
     assert L.tt_conf_unmask(ctypes.byref(p), None, 0, None) == 2
     # the same vocabulary without uniforms, or a vocabulary within the bound, is not refused for its size
     assert L.tt_conf_unmask(ctypes.byref(unmask_ok(B=256, S=16, V=big, logits_stride_row=big, logits=None)),
                             None, 0, None) == 1
-    ok = (1 << 21)
+    ok = 1 << 27
     assert L.tt_conf_unmask(ctypes.byref(unmask_ok(B=256, S=16, V=ok, logits_stride_row=ok, uniforms=FAKE,
                                                    logits=None)), None, 0, None) == 1
 
