@@ -56,8 +56,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 8;       // 32 query rows each; waves 0-3 load K, waves 4-7 load V
 constexpr int kThreads = 64 * kWaves;
-constexpr int kFinThreads = 256;
-constexpr int kFinChunks = kRows / (kFinThreads / 16);  // merge workgroups per pair
+constexpr int kFinRows = 16;   // rows per merge workgroup (16 threads per row), 4 in the eight-group form
 constexpr float kTau = 8.0f;  // lazy rescale threshold (log2 units)
 
 constexpr float kLn2 = 0.693147180559945309f;
@@ -925,20 +924,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
 // Merge the per-segment partials of every pair that segment boundaries cut,
 // and write O = 0, LSE = -inf for pairs with no keys at all. The pair's
 // segments follow from the unit counts the main kernel left in the workspace.
-// Grid: n_pairs * kFinChunks workgroups of PS * 256 threads, 16 rows each; a
-// row's 16 threads take D/16 consecutive elements each. Partials are read eight
-// at a time, every load of a group issued before any is used, and the next group
-// is in flight while one is merged. With PS > 1 (pairs cut into many pieces)
-// thread group q of the workgroup takes every PS-th partial from the q-th, and
-// group 0 merges the groups' results from LDS in group order; so a pair cut into
-// many segments costs few memory round trips.
-template <int D, bool F32, int PS>
-__global__ __launch_bounds__(kFinThreads * PS) void attn_bf16_finalize(Args a, const int* __restrict__ ctx_len) {
-    constexpr int RPW = kFinThreads / 16;   // rows per workgroup
+// Grid: n_pairs * (kRows / RPW) workgroups of PS thread groups of 16 RPW
+// threads, RPW rows each; a row's 16 threads take D/16 consecutive elements
+// each. Partials are read eight at a time, every load of a group issued before
+// any is used, and the next group is in flight while one is merged. With PS > 1
+// (pairs cut into many pieces) thread group q of the workgroup takes every
+// PS-th partial from the q-th, and group 0 merges the groups' results from LDS
+// in group order; so a pair cut into many segments costs few memory round
+// trips (with eight groups, up to 64 partials in one).
+template <int D, bool F32, int PS, int RPW>
+__global__ __launch_bounds__(16 * RPW * PS) void attn_bf16_finalize(Args a, const int* __restrict__ ctx_len) {
+    constexpr int GT = 16 * RPW;            // threads per group
+    constexpr int CH = kRows / RPW;         // workgroups per pair
     constexpr int EPT = D / 16;             // elements per thread
     constexpr int NG = F32 && PS > 1 ? 4 : 8;  // partials per group (fp32 ones in four at most 128 registers)
     const int mult = a.Hkv * a.n_rb;
-    const int p = blockIdx.x / kFinChunks, chunk = blockIdx.x % kFinChunks;
+    const int p = blockIdx.x / CH, chunk = blockIdx.x % CH;
     const int b = p / mult, pl = p % mult;
     const int g = pl / a.n_rb, rb = pl % a.n_rb;
     const int W = a.units_before[0];
@@ -952,8 +953,8 @@ __global__ __launch_bounds__(kFinThreads * PS) void attn_bf16_finalize(Args a, c
         s1 = (U + units - 1) / seg_len;
         if (s0 == s1) return;  // written by the main kernel
     }
-    const int grp = threadIdx.x / kFinThreads;  // partial group (PS > 1)
-    const int tid = threadIdx.x % kFinThreads;
+    const int grp = threadIdx.x / GT;  // partial group (PS > 1)
+    const int tid = threadIdx.x % GT;
     const int rl = chunk * RPW + tid / 16;  // row within the block
     const int rr = rb * kRows + rl;
     const bool live = rr < a.S * a.G;
@@ -1022,8 +1023,8 @@ __global__ __launch_bounds__(kFinThreads * PS) void attn_bf16_finalize(Args a, c
     }
     if constexpr (PS > 1) {
         // groups 1..PS-1 hand (M, Wsum, acc) to group 0, which merges them in group order
-        __shared__ float xm[PS - 1][kFinThreads], xw[PS - 1][kFinThreads];
-        __shared__ f32xE xa[PS - 1][kFinThreads];
+        __shared__ float xm[PS - 1][GT], xw[PS - 1][GT];
+        __shared__ f32xE xa[PS - 1][GT];
         if (grp > 0) {
             xm[grp - 1][tid] = M;
             xw[grp - 1][tid] = Wsum;
@@ -1103,9 +1104,10 @@ AttnPlan plan_attn_bf16(const tt_block_attn_params& p, int n_cu) {
     pl.ws_part_lse = (size_t)pl.n_slots * kRows * sizeof(float);
     pl.ws_units = ((size_t)(p.B + 1) * sizeof(int) + 255) / 256 * 256;
     pl.ws_total = pl.ws_part_o + pl.ws_part_lse + pl.ws_units + 256;
-    // pairs cut into many pieces on average (16 or more): the merge splits each
-    // pair's partials over four thread groups
-    pl.fin_split = (long long)pl.n_seg >= 16LL * pl.n_pairs ? 4 : 1;
+    // pairs cut into many pieces on average: the merge splits each pair's
+    // partials over four thread groups (16 or more pieces), or eight of four rows
+    // each (32 or more)
+    pl.fin_split = (long long)pl.n_seg >= 32LL * pl.n_pairs ? 8 : ((long long)pl.n_seg >= 16LL * pl.n_pairs ? 4 : 1);
     return pl;
 }
 
@@ -1144,28 +1146,29 @@ tt_status launch_attn_bf16(const tt_block_attn_params& p, const AttnPlan& pl, vo
         while ((1 << a.page_shift) < p.page_size) ++a.page_shift;
     }
     const bool p2 = a.page_shift >= 0;
-    const dim3 grid(pl.n_seg), blk(kThreads), fgrid(pl.n_pairs * kFinChunks), fblk(kFinThreads),
-        fblk4(4 * kFinThreads);
+    const dim3 grid(pl.n_seg), blk(kThreads);
+    auto merge = [&](auto D_) {
+        constexpr int D = decltype(D_)::value;
+        const dim3 g16(pl.n_pairs * (kRows / kFinRows)), g4(pl.n_pairs * (kRows / 4));
+        if (pl.fin_split == 8) {
+            if (a.o_f32) hipLaunchKernelGGL((attn_bf16_finalize<D, true, 8, 4>), g4, dim3(8 * 64), 0, s, a, a.ctx_len);
+            else hipLaunchKernelGGL((attn_bf16_finalize<D, false, 8, 4>), g4, dim3(8 * 64), 0, s, a, a.ctx_len);
+        } else if (pl.fin_split == 4) {
+            if (a.o_f32) hipLaunchKernelGGL((attn_bf16_finalize<D, true, 4, kFinRows>), g16, dim3(4 * 16 * kFinRows), 0, s, a, a.ctx_len);
+            else hipLaunchKernelGGL((attn_bf16_finalize<D, false, 4, kFinRows>), g16, dim3(4 * 16 * kFinRows), 0, s, a, a.ctx_len);
+        } else {
+            if (a.o_f32) hipLaunchKernelGGL((attn_bf16_finalize<D, true, 1, kFinRows>), g16, dim3(16 * kFinRows), 0, s, a, a.ctx_len);
+            else hipLaunchKernelGGL((attn_bf16_finalize<D, false, 1, kFinRows>), g16, dim3(16 * kFinRows), 0, s, a, a.ctx_len);
+        }
+    };
     if (p.head_dim == 128) {
         if (p2) hipLaunchKernelGGL((attn_bf16_kernel<128, true>), grid, blk, 0, s, a, a.page_table, a.ctx_len);
         else hipLaunchKernelGGL((attn_bf16_kernel<128, false>), grid, blk, 0, s, a, a.page_table, a.ctx_len);
-        if (pl.fin_split > 1) {
-            if (a.o_f32) hipLaunchKernelGGL((attn_bf16_finalize<128, true, 4>), fgrid, fblk4, 0, s, a, a.ctx_len);
-            else hipLaunchKernelGGL((attn_bf16_finalize<128, false, 4>), fgrid, fblk4, 0, s, a, a.ctx_len);
-        } else {
-            if (a.o_f32) hipLaunchKernelGGL((attn_bf16_finalize<128, true, 1>), fgrid, fblk, 0, s, a, a.ctx_len);
-            else hipLaunchKernelGGL((attn_bf16_finalize<128, false, 1>), fgrid, fblk, 0, s, a, a.ctx_len);
-        }
+        merge(std::integral_constant<int, 128>{});
     } else {
         if (p2) hipLaunchKernelGGL((attn_bf16_kernel<64, true>), grid, blk, 0, s, a, a.page_table, a.ctx_len);
         else hipLaunchKernelGGL((attn_bf16_kernel<64, false>), grid, blk, 0, s, a, a.page_table, a.ctx_len);
-        if (pl.fin_split > 1) {
-            if (a.o_f32) hipLaunchKernelGGL((attn_bf16_finalize<64, true, 4>), fgrid, fblk4, 0, s, a, a.ctx_len);
-            else hipLaunchKernelGGL((attn_bf16_finalize<64, false, 4>), fgrid, fblk4, 0, s, a, a.ctx_len);
-        } else {
-            if (a.o_f32) hipLaunchKernelGGL((attn_bf16_finalize<64, true, 1>), fgrid, fblk, 0, s, a, a.ctx_len);
-            else hipLaunchKernelGGL((attn_bf16_finalize<64, false, 1>), fgrid, fblk, 0, s, a, a.ctx_len);
-        }
+        merge(std::integral_constant<int, 64>{});
     }
     return hipGetLastError() == hipSuccess ? TT_OK : TT_ERR_HIP;
 }

@@ -34,7 +34,7 @@ struct AttnPlan {
     size_t ws_part_lse;  // bytes of partial LSE
     size_t ws_units;     // bytes of the per-sequence unit offsets the merge reads
     size_t ws_total;
-    int fin_split;       // thread groups the merge kernel splits a pair's partials over (1 or 4)
+    int fin_split;       // thread groups the merge kernel splits a pair's partials over (1, 4 or 8)
 };
 
 AttnPlan plan_attn_bf16(const tt_block_attn_params& p, int n_cu);

@@ -70,16 +70,18 @@ def pieces_per_pair(c, n_cu, piece_cost=3, tile=64, rows=256):
 def test_merge_group_boundaries():
     """Pairs cut into 2, 8, 9, 16, 17 and 24-25 pieces: the merge reads partials eight
     at a time with the next group in flight, so these are its group edges (one group,
-    a full group, a second group, two full groups, a third)."""
+    a full group, a second group, two full groups, a third). With 32 or more pieces per
+    pair the merge splits a pair's partials over eight thread groups: 40 pieces (five
+    each), 64 (eight each, one batch) and 65 (a second batch in the first group)."""
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     found = {}
-    for L in range(64, 8192, 16):
+    for L in range(64, 16384, 16):
         c = case(1, 16, 32, 2, 128, [L])
         for k in pieces_per_pair(c, n_cu):
-            for want in (2, 8, 9, 16, 17, 24, 25):
+            for want in (2, 8, 9, 16, 17, 24, 25, 40, 64, 65):
                 if k == want and want not in found:
                     found[want] = L
-    assert {8, 9, 16, 17}.issubset(found), found
+    assert {8, 9, 16, 17, 40, 64, 65}.issubset(found), found
     for want, L in sorted(found.items()):
         c = case(1, 16, 32, 2, 128, [L])
         print(want, L, run_full(c, what=f"{want} pieces, prefix {L}"))
