@@ -93,6 +93,28 @@ def test_merge_group_boundaries():
     print("single, fp32 output", check_attn(O, Ls, Or, Lr, c.dtype, "single fp32 out"))
 
 
+@pytest.mark.parametrize("kind", ["uniform_80", "one_short_80", "below_max", "uniform_odd"])
+def test_equal_and_unequal_lengths(kind):
+    """Batches whose sequences all have max_ctx_len keys and batches that miss it by little:
+    80 equal sequences (the segment scan reads ctx_len in two chunks of 64), the same with one
+    shorter sequence in the second chunk, equal sequences just below max_ctx_len (within the
+    page table's capacity), and an equal odd length with pairs cut into many pieces."""
+    if kind == "uniform_80":
+        c, mx = case(80, 2, 8, 2, 64, [200] * 80, page_size=16, shuffle_pages=True), None
+    elif kind == "one_short_80":
+        ctx = [200] * 80
+        ctx[70] = 150
+        c, mx = case(80, 2, 8, 2, 64, ctx, page_size=16, shuffle_pages=True), None
+    elif kind == "below_max":
+        c, mx = case(3, 16, 32, 2, 128, [300] * 3, page_size=16, shuffle_pages=True), 304
+    else:
+        c, mx = case(2, 16, 32, 2, 128, [1999] * 2, page_size=32, shuffle_pages=True), None
+    inp = synth.make_attn_inputs(c, seed=5)
+    O, L = gpu_attn(inp, max_ctx_len=mx)
+    Or, Lr = oracle_attn(inp)
+    print(kind, check_attn(O, L, Or, Lr, c.dtype, kind))
+
+
 def test_ragged_bf16_full_size():
     """B=64, prefix 16*U{32..512}, shuffled 16-token pages: every row at full size."""
     c = synth.attn_case("ragged")
