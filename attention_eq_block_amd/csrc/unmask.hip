@@ -353,8 +353,9 @@ __global__ __launch_bounds__(256) void sample_locate(UArgs a) {
     }
     // pass 1: region totals, NQ iterations of loads in flight per wave (lanes past
     // the split's end load its last chunk again and count nothing, so every load
-    // is unconditional and they issue together)
-    constexpr int NQ = BF16 ? 16 : 8;
+    // is unconditional and they issue together). One round covers 4 NQ
+    // iterations, 16384 logits: every split a drawing step plans, up to V = 2^20.
+    constexpr int NQ = BF16 ? 8 : 4;
     u32x4 keep0[NQ], keep1[NQ];  // this wave's chunks of the last round of loads
     for (int G0 = w; G0 < NI; G0 += 4 * NQ) {
 #pragma unroll
