@@ -355,7 +355,7 @@ __global__ __launch_bounds__(256) void sample_locate(UArgs a) {
     // the split's end load its last chunk again and count nothing, so every load
     // is unconditional and they issue together). One round covers 4 NQ
     // iterations, 16384 logits: every split a drawing step plans, up to V = 2^20.
-    constexpr int NQ = BF16 ? 8 : 4;
+    constexpr int NQ = 8;
     u32x4 keep0[NQ], keep1[NQ];  // this wave's chunks of the last round of loads
     for (int G0 = w; G0 < NI; G0 += 4 * NQ) {
 #pragma unroll
