@@ -301,25 +301,41 @@ __global__ __launch_bounds__(256) void sample_locate(UArgs a) {
     if (tid < a.n_vsplit) *reinterpret_cast<u32x4*>(&tri[tid]) = tr;
     if (tid == 128) sh_u = uu;
     __syncthreads();
-    if (tid == 0) {
-        float m = -INFINITY, z = 0.f;
-        int am = INT_MAX;
-        for (int k = 0; k < a.n_vsplit; ++k) combine(m, am, z, tri[k].m, tri[k].a, tri[k].z, c);
+    if (w == 0) {
+        // wave 0, one split per lane (n_vsplit <= 64): the row max, its first
+        // index (held by the first split whose max it is), the split weights
+        // 2^((m_k - m) c) z_k and their in-order scan, whose total is Z; the
+        // split where the scan passes u Z holds the draw
+        const bool in = lane < a.n_vsplit;
+        const float mk = in ? tri[lane].m : -INFINITY;
+        float m = mk;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+        const unsigned long long hm = __ballot(in && mk == m);
+        const int am = hm ? __shfl(in ? tri[lane].a : INT_MAX, __builtin_ctzll(hm)) : INT_MAX;
+        const float wk = m != -INFINITY && mk != -INFINITY ? tri[lane].z * __builtin_amdgcn_exp2f((mk - m) * c) : 0.f;
+        const float inc = wave_incl_scan(wk, lane);
+        float exc = __shfl_up(inc, 1);
+        if (lane == 0) exc = 0.f;
+        const float z = __shfl(inc, 63);
         float u = sh_u;
         u = u > 0.f ? fminf(u, 1.f) : 0.f;  // NaN and negatives count as 0
         const float t = u * z;
-        int kk = -1, klast = -1;
-        float W = 0.f, r = INFINITY;
+        int kk = -1;
+        float r = INFINITY;
         if (m != -INFINITY) {
-            for (int k = 0; k < a.n_vsplit; ++k) {
-                const float wk = tri[k].m == -INFINITY ? 0.f : tri[k].z * __builtin_amdgcn_exp2f((tri[k].m - m) * c);
-                if (wk > 0.f) klast = k;
-                if (kk < 0 && W + wk > t) { kk = k; r = t - W; }
-                W += wk;
+            const unsigned long long hit = __ballot(in && inc > t);
+            if (hit) {
+                kk = __builtin_ctzll(hit);
+                r = t - __shfl(exc, kk);
+            } else {  // not passed (u = 1, or rounding): the last split of nonzero weight
+                const unsigned long long hp = __ballot(wk > 0.f);
+                kk = hp ? 63 - __builtin_clzll(hp) : -1;
             }
-            if (kk < 0) kk = klast;
         }
-        sh_m = m; sh_z = z; sh_r = r; sh_k = kk; sh_am = am;
+        if (lane == 0) {
+            sh_m = m; sh_z = z; sh_r = r; sh_k = kk; sh_am = am;
+        }
     }
     __syncthreads();
     const int k = sh_k;
