@@ -23,6 +23,8 @@
 // their mean.
 #include <limits.h>
 
+#include <type_traits>
+
 #include "tt_internal.h"
 
 namespace tt {
@@ -230,6 +232,37 @@ __device__ __forceinline__ float dpp_move(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xF, false));
 }
 
+// Maximum over the 64 lanes of a wave (all active), in every lane: the same DPP
+// pattern as the scan below with max in place of the sum (the lanes a pattern
+// names none for take the identity), then lane 63's value.
+__device__ __forceinline__ int wave_max(int x) {
+    auto mv = [](int v, auto CTRL, auto ROWS) {
+        return __builtin_amdgcn_update_dpp(INT_MIN, v, decltype(CTRL)::value, decltype(ROWS)::value, 0xF, false);
+    };
+    using R = std::integral_constant<int, 0xF>;
+    x = max(x, mv(x, std::integral_constant<int, 0x111>{}, R{}));
+    x = max(x, mv(x, std::integral_constant<int, 0x112>{}, R{}));
+    x = max(x, mv(x, std::integral_constant<int, 0x114>{}, R{}));
+    x = max(x, mv(x, std::integral_constant<int, 0x118>{}, R{}));
+    x = max(x, mv(x, std::integral_constant<int, 0x142>{}, std::integral_constant<int, 0xA>{}));
+    x = max(x, mv(x, std::integral_constant<int, 0x143>{}, std::integral_constant<int, 0xC>{}));
+    return __builtin_amdgcn_readlane(x, 63);
+}
+__device__ __forceinline__ float wave_max(float x) {
+    auto mv = [](float v, auto CTRL, auto ROWS) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v),
+                                                          decltype(CTRL)::value, decltype(ROWS)::value, 0xF, false));
+    };
+    using R = std::integral_constant<int, 0xF>;
+    x = fmaxf(x, mv(x, std::integral_constant<int, 0x111>{}, R{}));
+    x = fmaxf(x, mv(x, std::integral_constant<int, 0x112>{}, R{}));
+    x = fmaxf(x, mv(x, std::integral_constant<int, 0x114>{}, R{}));
+    x = fmaxf(x, mv(x, std::integral_constant<int, 0x118>{}, R{}));
+    x = fmaxf(x, mv(x, std::integral_constant<int, 0x142>{}, std::integral_constant<int, 0xA>{}));
+    x = fmaxf(x, mv(x, std::integral_constant<int, 0x143>{}, std::integral_constant<int, 0xC>{}));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
 // Inclusive sum over the 64 lanes of a wave (all active), in a fixed tree order
 // (the same values give the same result in every call): prefix sums within each
 // row of 16 lanes by shifts of 1, 2, 4 and 8, then the total of row 0 added to
@@ -319,9 +352,7 @@ __global__ __launch_bounds__(256) void sample_locate(UArgs a) {
         // split where the scan passes u Z holds the draw
         const bool in = lane < a.n_vsplit;
         const float mk = in ? tri[lane].m : -INFINITY;
-        float m = mk;
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+        const float m = wave_max(mk);
         const unsigned long long hm = __ballot(in && mk == m);
         const int am = hm ? __shfl(in ? tri[lane].a : INT_MAX, __builtin_ctzll(hm)) : INT_MAX;
         const float wk = m != -INFINITY && mk != -INFINITY ? tri[lane].z * __builtin_amdgcn_exp2f((mk - m) * c) : 0.f;
@@ -414,9 +445,7 @@ __global__ __launch_bounds__(256) void sample_locate(UArgs a) {
                 if (G0 + 4 * q < NI) tot[1 + G0 + 4 * q] = incl[q];
         }
     }
-    int lp = lastpos;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) lp = max(lp, __shfl_xor(lp, off));
+    const int lp = wave_max(lastpos);
     if (lane == 0) wlast[w] = lp;
     __syncthreads();
     // the first region whose total takes the running sum past r: wave 0 scans the
