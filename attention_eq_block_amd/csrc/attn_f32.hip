@@ -30,15 +30,34 @@ struct F32Args {
     float scale;
 };
 
+// x of another lane by a DPP pattern (`id` where the pattern names none or the
+// row is masked off): a register move, no LDS round trip
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_move(float x, float id) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(__float_as_int(id), __float_as_int(x), CTRL, ROWS, 0xF, false));
+}
+
+// Sum and maximum over the 64 lanes of a wave (all active), in every lane: the
+// running value within each row of 16 lanes by shifts of 1, 2, 4 and 8, then
+// row 0's into row 1 and row 2's into row 3 (broadcast of lanes 15 and 47),
+// then that of rows 0-1 into rows 2 and 3 (broadcast of lane 31); lane 63 then
+// holds the result, which every lane reads.
+template <class Op>
+__device__ __forceinline__ float wave_reduce(float x, float id, Op op) {
+    x = op(x, dpp_move<0x111, 0xF>(x, id));  // row_shr:1
+    x = op(x, dpp_move<0x112, 0xF>(x, id));  // row_shr:2
+    x = op(x, dpp_move<0x114, 0xF>(x, id));  // row_shr:4
+    x = op(x, dpp_move<0x118, 0xF>(x, id));  // row_shr:8
+    x = op(x, dpp_move<0x142, 0xA>(x, id));  // row_bcast:15, rows 1 and 3
+    x = op(x, dpp_move<0x143, 0xC>(x, id));  // row_bcast:31, rows 2 and 3
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-    return x;
+    return wave_reduce(x, 0.f, [](float u, float v) { return u + v; });
 }
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-    return x;
+    return wave_reduce(x, -INFINITY, [](float u, float v) { return fmaxf(u, v); });
 }
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
