@@ -33,12 +33,24 @@ struct AppendArgs {
     int* status;
 };
 
-__device__ __forceinline__ int wave_incl_sum(int x, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
+// x of another lane by a DPP pattern (0 where the pattern names none or the
+// row is masked off): a register move, no LDS round trip
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_move(int x) {
+    return __builtin_amdgcn_update_dpp(0, x, CTRL, ROWS, 0xF, false);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (all active): within each row
+// of 16 lanes by shifts of 1, 2, 4 and 8, then row 0's total into row 1 and row
+// 2's into row 3 (broadcast of lanes 15 and 47), then that of rows 0-1 into rows
+// 2 and 3 (broadcast of lane 31)
+__device__ __forceinline__ int wave_incl_sum(int x, int) {
+    x += dpp_move<0x111, 0xF>(x);  // row_shr:1
+    x += dpp_move<0x112, 0xF>(x);  // row_shr:2
+    x += dpp_move<0x114, 0xF>(x);  // row_shr:4
+    x += dpp_move<0x118, 0xF>(x);  // row_shr:8
+    x += dpp_move<0x142, 0xA>(x);  // row_bcast:15, rows 1 and 3
+    x += dpp_move<0x143, 0xC>(x);  // row_bcast:31, rows 2 and 3
     return x;
 }
 
