@@ -14,9 +14,10 @@
 // "Sampling"), kernel 1b (sample_locate): a row with uniform u draws from
 // softmax(x / temperature) by inverse transform sampling. The split masses of
 // kernel 1 locate the split in which the cumulative sum passes u * Z; one
-// workgroup re-reads only that split, each thread a contiguous run of it, and a
-// workgroup scan of the run sums names the thread that walks its run again to
-// the first element whose cumulative sum passes. The drawn token's probability
+// workgroup re-reads only that split in iterations of 64 consecutive chunks,
+// a scan of the iteration totals names the iteration where the sum passes, a
+// scan of its chunk sums names the lane, and that lane walks its chunk to the
+// first element whose cumulative sum passes. The drawn token's probability
 // replaces the greedy confidence in kernel 2.
 // The masked-diffusion loss L_MD (Eq. (4)) runs vocab_reduce at temperature 1
 // and a one-workgroup finish (nll_finish): lse - x[target] per masked row and
