@@ -85,7 +85,7 @@ def test_merge_group_boundaries():
     for want, L in sorted(found.items()):
         c = case(1, 16, 32, 2, 128, [L])
         print(want, L, run_full(c, what=f"{want} pieces, prefix {L}"))
-    # float32 output (fp32 partials) where the merge splits each pair over four thread groups
+    # float32 output (fp32 partials) where the merge splits each pair over eight thread groups
     c = synth.attn_case("single")
     inp = synth.make_attn_inputs(c, seed=2)
     O, Ls = gpu_attn(inp, o_dtype=torch.float32)
@@ -247,15 +247,19 @@ def test_head_dim_64(dtype):
 
 
 @pytest.mark.parametrize("o_dtype", [None, torch.float32])
-def test_head_dim_64_many_pieces(o_dtype):
-    """One sequence with a 4096-token prefix at head_dim 64: every pair is cut into about 33
-    pieces, so the merge splits each pair's partials over four thread groups (bf16 and fp32
-    partials)."""
-    c = case(1, 16, 32, 2, 64, [4096])
+@pytest.mark.parametrize("prefix", [2000, 4096])
+def test_head_dim_64_many_pieces(prefix, o_dtype):
+    """One sequence at head_dim 64 whose pairs are cut into many pieces: a 2000-token prefix
+    gives about 20 per pair (the merge splits each pair's partials over four thread groups), a
+    4096-token prefix about 33 (eight groups of four rows); bf16 and fp32 partials."""
+    c = case(1, 16, 32, 2, 64, [prefix])
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    k = pieces_per_pair(c, n_cu)
+    print("pieces per pair", k)
     inp = synth.make_attn_inputs(c, seed=4)
     O, L = gpu_attn(inp, o_dtype=o_dtype)
     Or, Lr = oracle_attn(inp)
-    print(check_attn(O, L, Or, Lr, c.dtype, f"d=64, 33 pieces, out {o_dtype}"))
+    print(check_attn(O, L, Or, Lr, c.dtype, f"d=64, prefix {prefix}, out {o_dtype}"))
 
 
 @pytest.mark.parametrize("page_size", [32, 48, 64, 256])
