@@ -50,7 +50,7 @@ def draw_append(seed):
                      short=short)
 
 
-@pytest.mark.parametrize("seed", range(50))
+@pytest.mark.parametrize("seed", range(200))
 def test_random_appends(seed):
     inp, info = draw_append(seed)
     ref = _oracle(inp)

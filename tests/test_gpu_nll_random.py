@@ -34,7 +34,7 @@ def draw_batch(seed):
     return x.to(dtype), t, m
 
 
-@pytest.mark.parametrize("seed", range(40))
+@pytest.mark.parametrize("seed", range(120))
 def test_random_batches(seed):
     x, t, m = draw_batch(seed)
     loss, ref = _check(x, t, m, f"seed {seed}: {tuple(x.shape)} {x.dtype} masked {int(m.sum())}")

@@ -44,7 +44,7 @@ def draw_step(seed):
     return x, tokens, mask, gamma, temperature, steps_left, uniforms
 
 
-@pytest.mark.parametrize("seed", range(60))
+@pytest.mark.parametrize("seed", range(300))
 def test_random_steps(seed):
     x, tokens, mask, gamma, temperature, steps_left, uniforms = draw_step(seed)
     what = (f"seed {seed}: {tuple(x.shape)} {x.dtype} gamma {gamma} T {temperature} "
