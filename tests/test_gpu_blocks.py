@@ -77,11 +77,12 @@ def _commit(gpu, ora, Kn, Vn, what):
     assert int(gpu["pool_count"].item()) == ora["pool_count"], f"{what}: pool count differs"
 
 
-@pytest.mark.parametrize("ctx0,D,page_size", [
-    ([0, 37, 160], 128, 16),        # an empty prefix, one mid-page, one page-aligned
-    ([5, 100, 0, 61], 64, 48),      # pages of 48 rows: each block ends at a new offset within a page
+@pytest.mark.parametrize("ctx0,D,page_size,draw", [
+    ([0, 37, 160], 128, 16, False),       # an empty prefix, one mid-page, one page-aligned
+    ([5, 100, 0, 61], 64, 48, False),     # pages of 48 rows: each block ends at a new offset within a page
+    ([23, 0, 64], 128, 32, True),         # tokens drawn at the temperature from caller uniforms
 ])
-def test_blocks_with_commit_append(ctx0, D, page_size):
+def test_blocks_with_commit_append(ctx0, D, page_size, draw):
     B = len(ctx0)
     seed = 50 + D + page_size
     layers = _states(ctx0, D, page_size, seed)
@@ -99,8 +100,9 @@ def test_blocks_with_commit_append(ctx0, D, page_size):
             x = synth.make_logits(ucase, seed=seed + j, step=r, spike=1.0 * r, targets=targets)
             # B is 3 or 4: one sequence with a decision closer than the confidences' float32
             # resolution is left out of the exact comparison, as in the single-step tests
+            u = synth.make_uniforms(B, S, seed=seed + j, step=r) if draw else None
             got, _, _ = check_unmask(x, mask, tokens, gamma=0.8, temperature=0.1, steps_left=STEPS - r + 1,
-                                     what=f"block {j} step {r}", max_fragile_frac=0.34)
+                                     what=f"block {j} step {r}", max_fragile_frac=0.34, uniforms=u)
             tokens = torch.from_numpy(got["tokens"])
             mask = torch.from_numpy(got["mask"])
             if int(mask.sum()) == 0:
