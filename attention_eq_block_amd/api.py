@@ -1,4 +1,4 @@
-"""Python face of libtwotower_attn: the three C-ABI calls on torch tensors.
+"""Python face of libtwotower_attn: its C-ABI calls on torch tensors.
 
 Argument marshalling only -- shapes, strides, device pointers and the current
 stream go to the library; every step of the computation runs in its HIP
