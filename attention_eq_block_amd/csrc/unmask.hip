@@ -615,47 +615,66 @@ __global__ __launch_bounds__(64) void unmask_select(UArgs a) {
 }
 
 // L_MD (section 2.2, Eq. (4)) from the (max, argmax, sum) triples of
-// vocab_reduce at temperature 1: one workgroup, a thread per row, in row
-// order; the loss sums in double, so it does not depend on the launch.
+// vocab_reduce at temperature 1: one workgroup of kNllThreads, thread t taking
+// rows t, t + kNllThreads, ... The target, the mask and every split's triple of
+// a row are requested before any is used, and a masked row's target logit as
+// soon as the target and mask have arrived, so a row costs two memory round
+// trips. Each thread sums its rows in row order, and the threads' sums are added
+// in a fixed order (wave shuffles, then the waves in turn), in double: the loss
+// does not depend on timing.
+constexpr int kNllThreads = 1024;
 template <bool BF16>
-__global__ __launch_bounds__(256) void nll_finish(UArgs a, const int* __restrict__ targets, float* nll, float* loss,
-                                                  int* count) {
+__global__ __launch_bounds__(kNllThreads) void nll_finish(UArgs a, const int* __restrict__ targets, float* nll,
+                                                          float* loss, int* count) {
     const long long rows = (long long)a.B * a.S;
     double sum = 0.0;
     int n = 0;
-    for (long long row = threadIdx.x; row < rows; row += blockDim.x) {
-        if (!a.mask_in[row]) continue;
+    for (long long row = threadIdx.x; row < rows; row += kNllThreads) {
+        const int y = targets[row];
+        const uint8_t mk = a.mask_in[row];
         float m = -INFINITY, z = 0.f;
         int am = INT_MAX;
-        for (int k = 0; k < a.n_vsplit; ++k) {
-            const Triple t = a.part[(long long)k * rows + row];
-            combine(m, am, z, t.m, t.a, t.z, a.c);
+        float xt = 0.f;
+        for (int k0 = 0; k0 < a.n_vsplit; k0 += 8) {
+            Triple t[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (k0 + j < a.n_vsplit) t[j] = a.part[(long long)(k0 + j) * rows + row];
+            if (k0 == 0 && mk && y >= 0 && y < a.V)  // unmasked rows are not read
+                xt = elem<BF16>(static_cast<const char*>(a.logits) + row * a.stride * (BF16 ? 2 : 4), y);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (k0 + j < a.n_vsplit) combine(m, am, z, t[j].m, t[j].a, t[j].z, a.c);
         }
-        const int y = targets[row];
-        float v = __builtin_nanf("");
-        if (y >= 0 && y < a.V) {
-            const char* rp = static_cast<const char*>(a.logits) + row * a.stride * (BF16 ? 2 : 4);
-            v = m + __logf(z) - elem<BF16>(rp, y);
-        }
+        if (!mk) continue;
+        const float v = y >= 0 && y < a.V ? m + __logf(z) - xt : __builtin_nanf("");
         if (nll) nll[row] = v;
         sum += (double)v;
         ++n;
     }
-    __shared__ double ss[256];
-    __shared__ int sn[256];
-    ss[threadIdx.x] = sum;
-    sn[threadIdx.x] = n;
-    __syncthreads();
-    for (int off = 128; off > 0; off >>= 1) {
-        if ((int)threadIdx.x < off) {
-            ss[threadIdx.x] += ss[threadIdx.x + off];
-            sn[threadIdx.x] += sn[threadIdx.x + off];
-        }
-        __syncthreads();
+    // each wave halves its sums six times, then wave 0 adds the 16 wave sums in order
+    for (int off = 32; off > 0; off >>= 1) {
+        sum += __shfl_down(sum, off);
+        n += __shfl_down(n, off);
     }
+    constexpr int kWavesNll = kNllThreads / 64;
+    __shared__ double ss[kWavesNll];
+    __shared__ int sn[kWavesNll];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (lane == 0) {
+        ss[w] = sum;
+        sn[w] = n;
+    }
+    __syncthreads();
     if (threadIdx.x == 0) {
-        *loss = sn[0] > 0 ? (float)(ss[0] / sn[0]) : 0.f;
-        if (count) *count = sn[0];
+        double t = 0.0;
+        int c = 0;
+        for (int k = 0; k < kWavesNll; ++k) {
+            t += ss[k];
+            c += sn[k];
+        }
+        *loss = c > 0 ? (float)(t / c) : 0.f;
+        if (count) *count = c;
     }
 }
 
@@ -745,10 +764,10 @@ tt_status launch_nll(const tt_masked_nll_params& p, const UnmaskPlan& pl, void* 
     const dim3 grid(p.B * p.S, pl.n_vsplit);
     if (p.dtype == TT_BF16) {
         hipLaunchKernelGGL(vocab_reduce<true>, grid, dim3(256), 0, s, a);
-        hipLaunchKernelGGL(nll_finish<true>, dim3(1), dim3(256), 0, s, a, p.targets, p.nll, p.loss, p.count);
+        hipLaunchKernelGGL(nll_finish<true>, dim3(1), dim3(kNllThreads), 0, s, a, p.targets, p.nll, p.loss, p.count);
     } else {
         hipLaunchKernelGGL(vocab_reduce<false>, grid, dim3(256), 0, s, a);
-        hipLaunchKernelGGL(nll_finish<false>, dim3(1), dim3(256), 0, s, a, p.targets, p.nll, p.loss, p.count);
+        hipLaunchKernelGGL(nll_finish<false>, dim3(1), dim3(kNllThreads), 0, s, a, p.targets, p.nll, p.loss, p.count);
     }
     return hipGetLastError() == hipSuccess ? TT_OK : TT_ERR_HIP;
 }
