@@ -24,7 +24,8 @@
  * Conventions shared by every call:
  *   - Pointers named as tensors are DEVICE pointers owned by the caller. The
  *     library allocates no device memory; scratch comes from a caller-owned
- *     workspace of at least tt_*_workspace_bytes(...) bytes.
+ *     workspace of at least tt_*_workspace_bytes(...) bytes, except in
+ *     tt_block_attn_noalloc, which uses a fixed array inside the library.
  *   - Calls are asynchronous on the caller's stream and never synchronise the
  *     host. A returned TT_OK means the work was enqueued.
  *   - Arguments are validated on the host before anything is launched; a
@@ -36,7 +37,8 @@
  *     multiples of 16 bytes; tt_conf_unmask takes any element-aligned rows.
  *   - Calls that share a workspace must not overlap in time (same stream or
  *     ordered streams). Calls with distinct workspaces are independent; the
- *     library keeps no state besides a per-device cache of the CU count.
+ *     library keeps no state besides a per-device cache of the CU count and,
+ *     for tt_block_attn_noalloc, each device's scratch array and its address.
  *   - No C++ exception crosses this interface.
  */
 #ifndef TWOTOWER_ATTN_H
