@@ -751,6 +751,33 @@ def copy_calibration():
                       "note": "median of 5; copy counts bytes read plus written"}))
 
 
+def gemm_reference(seconds):
+    """Dense bf16 GEMMs (8192 x 8192 x 8192 through torch.matmul, contiguous operands) back to back for
+    about `seconds`: a compute reference. Board power sampled while it runs gives the energy of dense
+    MFMA work on the box, beside that of the attention loop and of a plain HBM stream."""
+    n = 8192
+    x = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    y = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    z = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(x, y, out=z)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    iters = 0
+    t0 = time.perf_counter()
+    e0.record()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            torch.matmul(x, y, out=z)
+        iters += 20
+        torch.cuda.synchronize()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    print(json.dumps({"gemm": f"bf16 {n}x{n}x{n}", "iters": iters, "seconds": ms / 1e3,
+                      "tflops": 2 * n ** 3 * iters / (ms * 1e-3) / 1e12}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -767,6 +794,8 @@ def main():
     ap.add_argument("--no-configs", action="store_true",
                     help="loop workload only: skip the per-config lines of the other four workloads")
     ap.add_argument("--copy-calibration", action="store_true", help="run only the counter-reference copy")
+    ap.add_argument("--gemm-reference", type=float, default=0.0, metavar="SECONDS",
+                    help="run only dense bf16 GEMMs for this long (a compute reference for power readings)")
     ap.add_argument("--graph", action="store_true",
                     help="loop workload: replay each denoising step from a HIP graph instead of launching its calls "
                          "from the host (measured slower on MI355X)")
@@ -781,6 +810,9 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.gemm_reference > 0:
+        gemm_reference(args.gemm_reference)
         return
     stream = torch.cuda.current_stream()
     if args.workload == "loop":
