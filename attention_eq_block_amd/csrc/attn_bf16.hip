@@ -479,6 +479,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
     b0 = __builtin_amdgcn_readfirstlane(b0);
     pl0 = __builtin_amdgcn_readfirstlane(pl0);
     t0 = __builtin_amdgcn_readfirstlane(t0);
+    if (TT_UNLIKELY(a.dbg != nullptr)) {
+        // Debug mode: every LDS byte starts as all ones (a NaN in bf16, page id -1), so a
+        // read of LDS that no load or store of this call filled reaches the outputs or the
+        // flags. The barrier orders the fill before any wave's first load into LDS.
+        auto poison = [&](void* p, int bytes) __attribute__((always_inline)) {
+            for (int o = tid * 16; o < bytes; o += kThreads * 16)
+                *reinterpret_cast<u32x4*>(static_cast<uint8_t*>(p) + o) = u32x4{~0u, ~0u, ~0u, ~0u};
+        };
+        poison(kb0, C::TILEB);
+        poison(kb1, C::TILEB);
+        poison(vb0, C::TILEB);
+        poison(vb1, C::TILEB);
+        poison(pgs, (int)sizeof(pgs));
+        poison(qlds, (int)sizeof(qlds));
+        lds_barrier();
+    }
 
     Cur cc;  // tile being computed
     set_seq(cc, a, ctx_len, b0);

@@ -84,6 +84,15 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(F32Args a) {
         if (raw < 0 || raw > a.Lmax) atomicOr(a.dbg, TT_DEBUG_CTX_LEN);
     }
     const int n = L + (a.Kd ? a.S : 0);
+    if (a.dbg) {
+        // debug mode: this wave's LDS slots start as NaN, so a read of one that no store of
+        // this call filled reaches the output (the fences below order the fill first)
+        const float qnan = __builtin_nanf("");
+        for (int i = lane; i < D; i += 64) qs[w][i] = qnan;
+        for (int r = 0; r < 64; ++r)
+            for (int i = lane; i < D + 4; i += 64) vs[w][r][i] = qnan;
+        ps[w][lane] = qnan;
+    }
 
     // the query row, in this wave's LDS slot (read back as broadcasts)
     const float* qp = a.Q + b * a.qsb + s * a.qss + h * a.qsh;

@@ -129,8 +129,11 @@ const char* tt_status_string(tt_status status);
  * outside [0, max_ctx_len]) and TT_DEBUG_PAGE_ID (a page id outside
  * [0, num_pages) for a prefix token) into *debug_flags, a device int32 that
  * the caller zeroes beforehand and reads after the stream reaches the call.
- * The outputs are those of the clamped data either way. With debug_flags NULL
- * nothing is checked.
+ * The outputs are those of the clamped data either way. Debug mode also fills
+ * the kernels' LDS buffers with all-ones bytes (NaN, page id -1) before the
+ * call's first load into them, so a read of LDS that the call never filled
+ * would show in the outputs or the flags. With debug_flags NULL nothing is
+ * checked or filled.
  */
 typedef struct tt_block_attn_params {
     int32_t dtype;        /* tt_dtype of Q and K/V */

@@ -177,6 +177,35 @@ def test_out_of_range_lengths_and_page_ids(dtype):
     assert torch.equal(O2, O) and torch.equal(L2, L)
 
 
+@pytest.mark.parametrize("kind", ["tiny", "single", "ragged", "long", "edges", "d64", "pages48", "empty", "f32"])
+def test_debug_mode_lds_poison(kind):
+    """Debug mode first fills every LDS buffer of the call with all-ones bytes (NaN in bf16 and
+    fp32, page id -1). Outputs bit-identical to the call without debug mode and a zero flags
+    word show that no LDS byte is read before a load or store of the call filled it: a poisoned
+    read would put a NaN into O or LSE, or raise TT_DEBUG_PAGE_ID."""
+    cases = {
+        "tiny": lambda: synth.attn_case("tiny"),
+        "single": lambda: synth.attn_case("single"),
+        "ragged": lambda: synth.attn_case("ragged"),
+        "long": lambda: synth.attn_case("long"),
+        "edges": lambda: case(5, 16, 32, 2, 128, (15, 17, 63, 64, 65), shuffle_pages=True, spare_pages=3,
+                              poison_tail=True),
+        "d64": lambda: case(3, 16, 8, 2, 64, [100, 33, 512], shuffle_pages=True),
+        "pages48": lambda: case(3, 16, 32, 2, 128, [100, 700, 257], page_size=48, shuffle_pages=True),
+        "empty": lambda: case(3, 16, 32, 2, 128, [0, 300, 0], with_den=False),
+        "f32": lambda: case(2, 5, 6, 3, 128, [37, 130], dtype=torch.float32, shuffle_pages=True),
+    }
+    c = cases[kind]()
+    inp = synth.make_attn_inputs(c, seed=3)
+    O, L = gpu_attn(inp)
+    flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+    Od, Ld = gpu_attn(inp, debug_flags=flags)
+    assert int(flags.item()) == 0, f"{kind}: debug flags {int(flags.item())}"
+    assert torch.equal(Od, O), f"{kind}: O differs under the LDS fill"
+    assert torch.equal(Ld.isnan(), L.isnan()) and torch.equal(torch.nan_to_num(Ld), torch.nan_to_num(L)), \
+        f"{kind}: LSE differs under the LDS fill"
+
+
 # --------------------------------------------------------------------------- edge cases
 
 @pytest.mark.parametrize("ctx", [(0,), (0, 0, 5), (1,), (15, 17, 63, 64, 65), (129, 0, 200)])
