@@ -43,7 +43,11 @@ import hashlib
 import json
 import math
 import os
+import re
+import shutil
+import subprocess
 import sys
+import threading
 import time
 
 import torch
@@ -533,6 +537,9 @@ def run_loop(args, stream):
     }
     if sweep:
         res["config"]["gamma_sweep"] = sweep
+    if not args.no_power:
+        log("[bench] board power during the loop")
+        res["power"] = board_power(lambda: block(args.gamma, graph=use_graph))
     if not args.no_cpu:
         log("[bench] cpu baseline (oracle): one whole block")
         cb = cpu_baseline_loop(layers, [lg for lg in logits], case, ucase, steps_per_block, uniforms=unis)
@@ -545,6 +552,62 @@ def run_loop(args, stream):
                 for g, v in sweep.items()}
         res["cpu_baseline"] = cb
     return res, layers
+
+
+def parse_power_clock(text):
+    """(board watts or None, [shader clock in MHz of each GFX_n domain]) from the text that
+    `amd-smi metric --power --clock` prints for one GPU."""
+    m = re.search(r"SOCKET_POWER:\s+(\d+)\s*W", text)
+    clocks = [int(c) for c in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s+(\d+)\s*MHz", text)]
+    return (int(m.group(1)) if m else None), clocks
+
+
+def board_power(work, settle_s=3.0, samples=3):
+    """Board power and shader clocks while `work()` is called back to back on a second host thread:
+    `amd-smi metric --power --clock` read `samples` times after `settle_s` seconds, and the power cap
+    from `rocm-smi --showmaxpower`. Both tools only read counters. None if amd-smi is missing."""
+    exe = shutil.which("amd-smi")
+    if exe is None:
+        return None
+    stop = threading.Event()
+    errors = []
+
+    def runner():
+        try:
+            while not stop.is_set():
+                work()
+        except Exception as e:  # reported, and the readings dropped
+            errors.append(repr(e))
+
+    th = threading.Thread(target=runner, daemon=True)
+    watts, clocks = [], []
+    th.start()
+    try:
+        time.sleep(settle_s)
+        for _ in range(samples):
+            out = subprocess.run([exe, "metric", "--power", "--clock"], capture_output=True, text=True,
+                                 timeout=30).stdout
+            w, c = parse_power_clock(out)
+            if w is not None:
+                watts.append(w)
+            clocks += c
+            time.sleep(0.5)
+    finally:
+        stop.set()
+        th.join()
+        torch.cuda.synchronize()
+    if errors or not watts:
+        return None
+    cap = None
+    smi = shutil.which("rocm-smi")
+    if smi:
+        m = re.search(r"Max Graphics Package Power \(W\):\s*([\d.]+)",
+                      subprocess.run([smi, "--showmaxpower"], capture_output=True, text=True, timeout=30).stdout)
+        cap = float(m.group(1)) if m else None
+    return {"board_w": watts, "cap_w": cap,
+            "shader_mhz": {"min": min(clocks), "mean": sum(clocks) / len(clocks), "max": max(clocks)} if clocks
+            else None,
+            "sample": f"amd-smi, {samples} readings {settle_s:g} s into a run of the same blocks after the timed ones"}
 
 
 APPEND_METRIC = "committed-block KV rows appended per s (one layer); achieved HBM GB/s vs peak"
@@ -791,6 +854,8 @@ def main():
     ap.add_argument("--sample", action="store_true",
                     help="loop workload: draw tokens at the temperature (caller uniforms) instead of the argmax")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baselines")
+    ap.add_argument("--no-power", action="store_true",
+                    help="loop workload: skip the board power readings taken after the timed blocks")
     ap.add_argument("--no-configs", action="store_true",
                     help="loop workload only: skip the per-config lines of the other four workloads")
     ap.add_argument("--copy-calibration", action="store_true", help="run only the counter-reference copy")

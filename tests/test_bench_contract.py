@@ -22,3 +22,16 @@ def test_traffic_summary_is_plausible_or_withheld():
     import bench
     t = bench.measured_traffic()
     assert t is None or 0.9 * 277413888 < t < 1.5 * 277413888
+
+
+def test_power_clock_parsing():
+    """The board power readout takes SOCKET_POWER and the CLK of each GFX_n domain, not the
+    MIN/MAX limits nor the memory clock (text laid out as amd-smi prints it for one GPU)."""
+    sys.path.insert(0, ROOT)
+    import bench
+    text = ("GPU: 0\n    POWER:\n        SOCKET_POWER: 1385 W\n        GFX_VOLTAGE: N/A\n    CLOCK:\n"
+            "        GFX_0:\n            CLK: 1975 MHz\n            MIN_CLK: 500 MHz\n            MAX_CLK: 2400 MHz\n"
+            "        GFX_1:\n            CLK: 1918 MHz\n            MIN_CLK: 500 MHz\n"
+            "        MEM_0:\n            CLK: 2000 MHz\n            MIN_CLK: 2000 MHz\n")
+    assert bench.parse_power_clock(text) == (1385, [1975, 1918])
+    assert bench.parse_power_clock("no readings") == (None, [])
