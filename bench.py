@@ -599,6 +599,8 @@ def board_power(work, settle_s=3.0, samples=3):
                 watts.append(w)
             clocks += c
             time.sleep(0.5)
+    except (OSError, subprocess.SubprocessError) as e:  # a tool that fails or hangs: no readings
+        errors.append(repr(e))
     finally:
         stop.set()
         th.join()
@@ -608,9 +610,13 @@ def board_power(work, settle_s=3.0, samples=3):
     cap = None
     smi = shutil.which("rocm-smi")
     if smi:
-        m = re.search(r"Max Graphics Package Power \(W\):\s*([\d.]+)",
-                      subprocess.run([smi, "--showmaxpower"], capture_output=True, text=True, timeout=30).stdout)
-        cap = float(m.group(1)) if m else None
+        try:
+            m = re.search(r"Max Graphics Package Power \(W\):\s*([\d.]+)",
+                          subprocess.run([smi, "--showmaxpower"], capture_output=True, text=True,
+                                         timeout=30).stdout)
+            cap = float(m.group(1)) if m else None
+        except (OSError, subprocess.SubprocessError):
+            cap = None
     return {"board_w": watts, "cap_w": cap,
             "shader_mhz": {"min": min(clocks), "mean": sum(clocks) / len(clocks), "max": max(clocks)} if clocks
             else None,
