@@ -564,10 +564,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
     // Load pipeline: the K waves request tile i+1 and the V waves tile i at
     // the start of tile i's phase (V is used one tile later than K), and every
     // wave waits for its own loads before the barrier that ends the phase.
-    // Every issue loads a whole tile (past the segment's end it reloads the
-    // last one).
+    // Every issue loads a whole tile; once the segment's last tile is loaded
+    // (the K waves get there a phase before the V waves) an issue loads
+    // nothing, and the waits on vmcnt(0) need no count.
     Cur cl = cc;  // next tile to load
     int ul = 0;   // its index in the segment
+    bool all_loaded = false;
     int pg_base = 0;
     // The batch in use is also kept in a register (lane l: tile pg_base + l),
     // so a tile's id is a readlane and its LDS copy is read once per batch.
@@ -584,6 +586,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): here, not before every tile's readlane
             page_batch(cl, ul, 64, pbuf ^ 1);    // the batch after next, into the one used up
         }
+        if (TT_UNLIKELY(all_loaded)) return;
         const int page = __builtin_amdgcn_readlane(pgl, ul - pg_base);
         if (TT_UNLIKELY(a.dbg != nullptr) && is_prefix(cl, a) && (page < 0 || page >= a.num_pages) && lane == 0)
             atomicOr(a.dbg, TT_DEBUG_PAGE_ID);
@@ -595,6 +598,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Args a, const in
                 q_dma(cl);
                 q_tag = ul;
             }
+        } else {
+            all_loaded = true;
         }
     };
 
