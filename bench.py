@@ -604,7 +604,8 @@ def board_power(work, settle_s=3.0, samples=3):
     finally:
         stop.set()
         th.join()
-        torch.cuda.synchronize()
+        if torch.cuda.is_available():
+            torch.cuda.synchronize()
     if errors or not watts:
         return None
     cap = None

@@ -1,8 +1,10 @@
 """bench.py's command-line contract, on the CPU: more than one GPU is refused with exit code 2
-before anything touches a device, and the traffic summary it reports is plausible or withheld."""
+before anything touches a device, the traffic summary it reports is plausible or withheld, and the
+board power readout is parsed from the tools' text or withheld when they fail."""
 import os
 import subprocess
 import sys
+import time
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -35,3 +37,38 @@ def test_power_clock_parsing():
             "        MEM_0:\n            CLK: 2000 MHz\n            MIN_CLK: 2000 MHz\n")
     assert bench.parse_power_clock(text) == (1385, [1975, 1918])
     assert bench.parse_power_clock("no readings") == (None, [])
+
+
+def test_power_readout_withheld_when_the_tool_fails(monkeypatch):
+    """No amd-smi, or an amd-smi that fails or hangs, leaves the readout None instead of ending the
+    bench; the busy-work thread is stopped either way."""
+    sys.path.insert(0, ROOT)
+    import bench
+    calls = []
+    monkeypatch.setattr(bench.shutil, "which", lambda name: None)
+    assert bench.board_power(lambda: calls.append(1), settle_s=0.0) is None
+
+    def hang(*a, **k):
+        raise subprocess.TimeoutExpired(cmd="amd-smi", timeout=30)
+
+    monkeypatch.setattr(bench.shutil, "which", lambda name: "/usr/bin/" + name)
+    monkeypatch.setattr(bench.subprocess, "run", hang)
+    assert bench.board_power(lambda: time.sleep(0.001), settle_s=0.0) is None
+
+
+def test_power_readout_from_tool_text(monkeypatch):
+    """Readings parsed from the tools' text, the cap from rocm-smi."""
+    sys.path.insert(0, ROOT)
+    import bench
+    smi = ("GPU: 0\n    POWER:\n        SOCKET_POWER: 1399 W\n    CLOCK:\n        GFX_0:\n            CLK: 1990 MHz\n"
+           "        GFX_1:\n            CLK: 2010 MHz\n")
+    cap = "GPU[0]\t\t: Max Graphics Package Power (W): 1400.0\n"
+
+    def run(cmd, **k):
+        return subprocess.CompletedProcess(cmd, 0, stdout=cap if "--showmaxpower" in cmd else smi, stderr="")
+
+    monkeypatch.setattr(bench.shutil, "which", lambda name: "/usr/bin/" + name)
+    monkeypatch.setattr(bench.subprocess, "run", run)
+    r = bench.board_power(lambda: time.sleep(0.001), settle_s=0.0, samples=2)
+    assert r["board_w"] == [1399, 1399] and r["cap_w"] == 1400.0
+    assert r["shader_mhz"] == {"min": 1990, "mean": 2000.0, "max": 2010}
